@@ -1,0 +1,338 @@
+"""Pins of the oracle's dispatch/combine path against what the pages and the
+mathematics fix: the worked examples, the prefix-sum example, the byte model,
+the correctness invariants, brute force on tiny inputs, and closed forms."""
+
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from combine_router_softmax_expert_amd import workloads as wl
+from conftest import read_golden
+
+
+def _token_rows(T, H):
+    """Rows that identify their token: row t holds bf16(t + 1) in every channel."""
+    return np.repeat(wl.float32_to_bf16_bits(np.arange(1, T + 1, dtype=np.float32))[:, None], H, axis=1)
+
+
+# --------------------------------------------------------------------------
+# worked examples of the pages
+# --------------------------------------------------------------------------
+
+def test_worked_top2_example_receive_layout(orc):
+    recs = read_golden("ep_top2_worked_example.txt")
+    kv = {r[0]: r[1:] for r in recs if r[0] in ("ranks", "experts", "top_k", "tokens")}
+    P, E, k, T = (int(kv[n][0]) for n in ("ranks", "experts", "top_k", "tokens"))
+    ids = np.zeros((T, k), np.int32)
+    for r in recs:
+        if r[0] == "route":
+            ids[int(r[1])] = [int(v) for v in r[2:]]
+    w = np.full((T, k), 0.5, np.float32)
+    H = 8
+    sh = orc.Shape(P, T, E, k, H, False)
+    d = orc.dispatch(sh, _token_rows(T, H), ids, w)
+    Tp, Ep = T // P, E // P
+    got = {}
+    for e in range(E):
+        seg = d["recv_meta"][d["expert_off"][e]:d["expert_off"][e + 1]]
+        got[e] = [int(m["src_rank"]) * Tp + int(m["src_token"]) for m in seg]
+        # the payload row that arrived is the token's own row
+        rows = d["recv_rows"][d["expert_off"][e]:d["expert_off"][e + 1]].view(np.uint16)
+        assert np.array_equal(rows[:, 0], wl.float32_to_bf16_bits(np.float32(got[e]) + 1))
+    for r in recs:
+        if r[0] == "recv":
+            rank, e, toks = int(r[1]), int(r[2]), [int(v) for v in r[3:]]
+            assert got[e] == toks, (e, got[e], toks)
+            lo, hi = d["rank_recv_off"][rank], d["rank_recv_off"][rank + 1]
+            assert lo <= d["expert_off"][e] and d["expert_off"][e + 1] <= hi
+    # every rank sends T/P*k rows and, here, receives 4
+    assert np.array_equal(d["C"].sum(axis=1), np.full(P, Tp * k))
+    assert np.array_equal(np.diff(d["rank_recv_off"]), np.full(P, 4))
+    assert d["N"].sum() == T * k
+
+
+def test_prefix_sum_example(orc):
+    recs = {r[0]: [int(v) for v in r[1:]] for r in read_golden("ep_prefix_sum_example.txt")}
+    counts, offsets = recs["send_count"], recs["send_offset"]
+    P = len(counts)
+    # one source rank of 4 tokens x top-2 whose destinations are 0,0,0,1,2,2,3,3
+    # (one expert per rank, so expert == destination rank)
+    dests = [d for d, c in enumerate(counts) for _ in range(c)]
+    assert len(dests) == 8
+    rank0 = np.array([[0, 2], [0, 3], [0, 1], [2, 3]], np.int32)
+    assert sorted(rank0.ravel().tolist()) == dests
+    others = np.array([[1, 0], [2, 1], [3, 2], [0, 3]] * (P - 1), np.int32)
+    ids = np.concatenate([rank0, others])
+    T = ids.shape[0]
+    sh = orc.Shape(P, T, P, 2, 8, False)
+    d = orc.dispatch(sh, _token_rows(T, 8), ids, np.full((T, 2), 0.5, np.float32))
+    assert d["C"][0].tolist() == counts
+    assert (d["send_off"][0] - d["send_off"][0, 0]).tolist() == offsets
+
+
+def test_all_to_all_transpose_example(orc):
+    recs = read_golden("a2a_transpose_example.txt")
+    before = {int(r[1]): r[2:] for r in recs if r[0] == "before"}
+    after = {int(r[1]): r[2:] for r in recs if r[0] == "after"}
+    P = len(before)
+    # P ranks, P experts (one per rank), top-1, piece j of rank i routed to expert j;
+    # the row content encodes the piece name A_ij as 10*i + j
+    T = P * P
+    ids = np.array([[j] for i in range(P) for j in range(P)], np.int32)
+    names = [before[i][j] for i in range(P) for j in range(P)]
+    vals = np.array([10 * int(n[1]) + int(n[2]) for n in names], np.float32)
+    x = np.repeat(wl.float32_to_bf16_bits(vals)[:, None], 8, axis=1)
+    sh = orc.Shape(P, T, P, 1, 8, False)
+    d = orc.dispatch(sh, x, ids, np.ones((T, 1), np.float32))
+    for r in range(P):
+        lo, hi = d["rank_recv_off"][r], d["rank_recv_off"][r + 1]
+        got = wl.bf16_bits_to_float32(d["recv_rows"][lo:hi].view(np.uint16)[:, 0]).astype(int)
+        assert [f"A{v // 10}{v % 10}" for v in got] == after[r]
+
+
+def test_byte_model_closed_form(orc):
+    kv = {r[0]: int(r[1]) for r in read_golden("ep_byte_model.txt")}
+    w = wl.WORKLOADS["c3"]
+    assert (w.tokens, w.top_k, w.hidden) == (kv["tokens"], kv["top_k"], kv["hidden"])
+    sh = orc.Shape.of(w)
+    inp = wl.make_inputs(w)
+    ids, wt = orc.route(sh, inp["logits"])
+    d = orc.dispatch(sh, inp["x"], ids, wt, payload=False)
+    rows_sent = int(d["N"].sum())            # assignments that crossed the dispatch exchange
+    rows_back = int(np.unique(d["recv_pos"]).size)  # expert outputs that come back for combine
+    dispatch_bytes = rows_sent * sh.H * kv["dispatch_bytes_per_element"]
+    combine_bytes = rows_back * sh.H * kv["combine_bytes_per_element"]
+    total = dispatch_bytes + combine_bytes
+    assert total == 88_080_384
+    assert round(total / 1e6) == kv["about_megabytes"]
+    # the scales travel as well but are metadata: 4 bytes per 128 channels per row
+    assert rows_sent * (sh.H // 128) * 4 == 917_504
+
+
+# --------------------------------------------------------------------------
+# invariants of the page's correctness section, on every workload shape
+# --------------------------------------------------------------------------
+
+def _check_invariants(sh, ids, d):
+    P, T, E, k = sh.P, sh.T, sh.E, sh.k
+    Tp, Ep, Na = T // P, E // P, T * k
+    # assignment conservation
+    assert d["N"].sum() == Na and d["n"].sum() == Na
+    assert np.array_equal(d["N"], np.bincount(ids.ravel(), minlength=E))
+    # positions are permutations (each assignment sent once, received once)
+    assert np.array_equal(np.sort(d["send_pos"].ravel()), np.arange(Na))
+    assert np.array_equal(np.sort(d["recv_pos"].ravel()), np.arange(Na))
+    # the handle that arrives brings each assignment back to its token and slot
+    m = d["recv_meta"][d["recv_pos"].ravel()]
+    t = np.repeat(np.arange(T), k)
+    j = np.tile(np.arange(k), T)
+    assert np.array_equal(m["src_rank"].astype(np.int64) * Tp + m["src_token"], t)
+    assert np.array_equal(m["slot"], j)
+    assert np.array_equal(m["local_expert"], ids.ravel() % Ep)
+    # ownership: every row of rank r's receive region belongs to an expert of r
+    for r in range(P):
+        lo, hi = d["rank_recv_off"][r], d["rank_recv_off"][r + 1]
+        seg_e = np.searchsorted(d["expert_off"], np.arange(lo, hi), side="right") - 1
+        assert np.all(seg_e // Ep == r)
+        assert np.array_equal(seg_e % Ep, d["recv_meta"]["local_expert"][lo:hi])
+    # send region of rank s holds exactly its assignments, destination-contiguous
+    src_of_row = np.repeat(np.arange(P), Tp * k)
+    assert np.array_equal(src_of_row[d["send_pos"].ravel()], t // Tp)
+    for s in range(P):
+        for r in range(P):
+            lo = d["send_off"][s, r * Ep]
+            assert d["C"][s, r] == sum(d["n"][s, r * Ep:(r + 1) * Ep])
+            rows = np.arange(lo, lo + d["C"][s, r])
+            dest = d["send_meta"]["local_expert"][rows]
+            assert np.all(np.diff(dest) >= 0)  # bucketed by local expert
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_invariants_on_workloads(orc, name):
+    w = wl.WORKLOADS[name]
+    sh = orc.Shape.of(w)
+    logits = wl.make_logits(w.seed, w.tokens, w.num_experts, w.zipf)
+    ids, wt = orc.route(sh, logits)
+    x = np.zeros((w.tokens, w.hidden), np.uint16)
+    d = orc.dispatch(sh, x, ids, wt, payload=False)
+    _check_invariants(sh, ids, d)
+
+
+def _brute_positions(P, T, k, ids):
+    """Positions from their definition: the receive buffer is all assignments in
+    (expert, token) order; the send buffer is rank s's assignments in (expert,
+    token) order after the rows of ranks < s."""
+    Tp = T // P
+    send = np.zeros((T, k), np.int64)
+    recv = np.zeros((T, k), np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            before = [(t2, j2) for t2 in range(T) for j2 in range(k)
+                      if ids[t2, j2] < e or (ids[t2, j2] == e and t2 < t)]
+            recv[t, j] = len(before)
+            send[t, j] = (t // Tp) * Tp * k + sum(1 for (t2, _) in before if t2 // Tp == t // Tp)
+    return send, recv
+
+
+def test_positions_brute_force_all_routings(orc):
+    # P=2, E=4, k=2, 2 tokens per rank: every one of the C(4,2)^4 = 1296 routings
+    P, E, k, T = 2, 4, 2, 4
+    pairs = list(itertools.combinations(range(E), 2))
+    sh = orc.Shape(P, T, E, k, 8, False)
+    x = np.zeros((T, 8), np.uint16)
+    w = np.full((T, k), 0.5, np.float32)
+    for n, combo in enumerate(itertools.product(pairs, repeat=T)):
+        ids = np.array([c if (n >> t) & 1 else c[::-1] for t, c in enumerate(combo)], np.int32)
+        d = orc.dispatch(sh, x, ids, w, payload=False)
+        bs, br = _brute_positions(P, T, k, ids)
+        assert np.array_equal(d["send_pos"], bs) and np.array_equal(d["recv_pos"], br)
+
+
+@pytest.mark.parametrize("P,Tp,E,k", [(1, 7, 4, 2), (3, 5, 6, 3), (4, 3, 8, 1), (2, 9, 8, 8)])
+def test_positions_brute_force_random(orc, P, Tp, E, k):
+    rng = np.random.default_rng(P * 100 + Tp)
+    T = P * Tp
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
+    sh = orc.Shape(P, T, E, k, 8, False)
+    d = orc.dispatch(sh, np.zeros((T, 8), np.uint16), ids, np.ones((T, k), np.float32), payload=False)
+    bs, br = _brute_positions(P, T, k, ids)
+    assert np.array_equal(d["send_pos"], bs) and np.array_equal(d["recv_pos"], br)
+    _check_invariants(sh, ids, d)
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+
+def test_route_selection_brute_force_with_ties(orc):
+    rng = np.random.default_rng(5)
+    for E in (2, 3, 5, 8, 16):
+        for k in range(1, min(E, 8) + 1):
+            T = 64
+            logits = rng.integers(-3, 4, size=(T, E)).astype(np.float32)  # many ties
+            sh = orc.Shape(1, T, E, k, 8, False)
+            ids, _ = orc.route(sh, logits)
+            for t in range(T):
+                l = logits[t]
+                # rank of e: experts strictly better, or equal with a lower id
+                rank = np.array([np.sum(l > l[e]) + np.sum((l == l[e]) & (np.arange(E) < e)) for e in range(E)])
+                sel = np.argsort(rank)[:k]
+                assert ids[t].tolist() == sel.tolist()
+
+
+def test_route_weights_special_cases(orc):
+    rng = np.random.default_rng(6)
+    T, E = 256, 16
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    # k = 1: the renormalised weight is exactly 1
+    ids, w = orc.route(orc.Shape(1, T, E, 1, 8, False), logits)
+    assert np.all(w == 1.0) and np.array_equal(ids[:, 0], np.argmax(logits, axis=1))
+    # k = E: the weights are the full softmax (scipy, float64, rounded to float32)
+    ids, w = orc.route(orc.Shape(1, T, E, E, 8, False), logits)
+    full = softmax(logits.astype(np.float64), axis=1)
+    ref = np.take_along_axis(full, ids, axis=1).astype(np.float32)
+    assert np.max(np.abs(w - ref) / ref) <= 2.0 ** -23
+    # any k: renormalising the softmax over the chosen experts is the softmax of
+    # the chosen logits alone
+    for k in (2, 4, 8):
+        ids, w = orc.route(orc.Shape(1, T, E, k, 8, False), logits)
+        ref = softmax(np.take_along_axis(logits, ids, axis=1).astype(np.float64), axis=1).astype(np.float32)
+        assert np.max(np.abs(w - ref) / ref) <= 2.0 ** -23
+        assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1.0) < 1e-6)
+        assert np.all(np.diff(w, axis=1) <= 0)  # slot 0 is the most probable expert
+    # closed form: logits (0, ln 3) give weights (1/4, 3/4)
+    ids, w = orc.route(orc.Shape(1, 1, 2, 2, 8, False), np.float32([[0.0, np.log(3.0)]]))
+    assert ids.tolist() == [[1, 0]]
+    assert abs(w[0, 0] - 0.75) < 1e-7 and abs(w[0, 1] - 0.25) < 1e-7
+
+
+# --------------------------------------------------------------------------
+# stub and combine closed forms
+# --------------------------------------------------------------------------
+
+def test_combine_of_dispatch_is_identity_for_top1_expert0(orc):
+    # k = 1, every token to expert 0: the stub multiplies by 1 + 0/E = 1 and the
+    # weight is 1, so combine(stub(dispatch(x))) must give x back bit for bit
+    P, Tp, E, H = 4, 33, 8, 136
+    T = P * Tp
+    x = wl.make_hidden(21, T, H)
+    sh = orc.Shape(P, T, E, 1, H, False)
+    out = orc.run(sh, x, ids=np.zeros((T, 1), np.int32), w=np.ones((T, 1), np.float32))
+    assert np.array_equal(out["y"], x)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_combine_closed_form(orc, name):
+    # Straight from each token, with no permutation at all:
+    # y_t = sum_j w_tj * stub(x_t, e_tj).  The oracle goes through count, pack,
+    # exchange, stub, reverse exchange and reduce; a wrong offset that adds
+    # another token's output in fails this.
+    w_ = wl.WORKLOADS[name]
+    sh = orc.Shape.of(w_)
+    inp = wl.make_inputs(w_)
+    out = orc.run(sh, inp["x"], inp["logits"])
+    ids, w = out["ids"], out["w"]
+    T, k, H, E = sh.T, sh.k, sh.H, sh.E
+    if sh.fp8:
+        deq = np.empty((T, H), np.float32)
+        for t in range(T):
+            q, sc = orc.quantize_row(H, inp["x"][t])
+            deq[t] = orc.e4m3_to_f32(q) * np.repeat(sc, 128)     # fp32 product
+    else:
+        deq = wl.bf16_bits_to_float32(inp["x"])
+    ref = np.zeros((T, H))
+    mag = np.zeros((T, H))
+    for j in range(k):
+        m = ((E + ids[:, j]) / E).astype(np.float32)             # 1 + e/E, exact for power-of-two E
+        stub = wl.bf16_bits_to_float32(orc.bf16_from_double((deq * m[:, None]).astype(np.float64)))
+        ref += w[:, j].astype(np.float64)[:, None] * stub.astype(np.float64)
+        mag += np.abs(w[:, j].astype(np.float64)[:, None] * stub.astype(np.float64))
+    assert np.array_equal(out["y64"], ref)
+    # fp32 slot-order accumulation stays within its error bound of the exact sum
+    assert np.all(np.abs(out["y32"] - ref) <= k * 2.0 ** -24 * mag + 1e-300)
+    # y is y32 rounded once to bf16
+    assert np.array_equal(out["y"], orc.bf16_from_double(out["y32"].astype(np.float64)))
+
+
+def test_stub_closed_form_bf16(orc):
+    P, Tp, E, k, H = 2, 16, 8, 2, 64
+    T = P * Tp
+    sh = orc.Shape(P, T, E, k, H, False)
+    x = wl.make_hidden(31, T, H)
+    rng = np.random.default_rng(7)
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
+    d = orc.dispatch(sh, x, ids, np.full((T, k), 0.5, np.float32))
+    out = orc.stub(sh, d["expert_off"], d["recv_rows"], None)
+    for e in range(E):
+        lo, hi = d["expert_off"][e], d["expert_off"][e + 1]
+        xin = wl.bf16_bits_to_float32(d["recv_rows"][lo:hi].view(np.uint16)).astype(np.float64)
+        # x * (1 + e/E) is exact in float64; one rounding to bf16
+        assert np.array_equal(out[lo:hi], orc.bf16_from_double(xin * (1.0 + e / E)))
+
+
+# --------------------------------------------------------------------------
+# routing statistics of the synthetic workloads
+# --------------------------------------------------------------------------
+
+def test_uniform_count_matrix_statistics(orc):
+    # with uniform routing C_ij is close to N_a / P^2
+    w = wl.WORKLOADS["c4"]
+    sh = orc.Shape.of(w)
+    ids, wt = orc.route(sh, wl.make_logits(w.seed, w.tokens, w.num_experts))
+    d = orc.dispatch(sh, np.zeros((w.tokens, w.hidden), np.uint16), ids, wt, payload=False)
+    mean = sh.Na / sh.P ** 2
+    assert np.all(np.abs(d["C"] - mean) < 6 * np.sqrt(mean))
+    assert abs(np.trace(d["C"]) / sh.Na - 1 / sh.P) < 0.01   # local share ~ 1/P
+
+
+def test_skewed_workload_hot_expert_share(orc):
+    w = wl.WORKLOADS["c5"]
+    sh = orc.Shape.of(w)
+    ids, _ = orc.route(sh, wl.make_logits(w.seed, w.tokens, w.num_experts, w.zipf))
+    n = np.sort(np.bincount(ids.ravel(), minlength=w.num_experts))[::-1]
+    share = n[: w.num_experts // 10].sum() / n.sum()
+    assert 0.40 <= share <= 0.50
+    assert n.min() > 0
