@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-parallel dispatch/combine path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+route (softmax/top-k), dispatch (count, scan, pack, exchange), expert stub,
+combine (reverse exchange, weighted reduction).  The default workload is the
+decode-shaped H=7168 / E=256 / top-8 batch (8 logical ranks x 16 tokens);
+``--config`` selects another of the five workloads.
+
+Prints ONE JSON line: tokens/s over K back-to-back steps with the inputs
+resident in HBM, the per-phase split, the roofline of the dominant kernel
+(algorithmic bytes per launch / its mean HIP-event duration, against the
+8 TB/s HBM peak) and the CPU oracle's rate on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s vs peak, H=7168 E=256 k=8"
+
+KERNEL_SOURCES = {
+    "route_topk": "route.hip", "count": "count.hip", "scan": "count.hip", "pack": "pack.hip",
+    "exchange": "exchange.hip", "stub": "stub.hip", "reverse_exchange": "exchange.hip", "reduce": "reduce.hip",
+}
+PHASE_OF = {
+    "route_topk": "route", "count": "dispatch", "scan": "dispatch", "pack": "dispatch", "exchange": "dispatch",
+    "stub": "expert_stub", "reverse_exchange": "combine", "reduce": "combine",
+}
+
+
+def kernel_bytes(w) -> dict:
+    """Algorithmic bytes one launch of each kernel moves (payload model: hidden rows,
+    FP8 scales and routing data; the 16-byte handle records and int32 position
+    arrays are metadata, counted separately)."""
+    T, E, k, H = w.tokens, w.num_experts, w.top_k, w.hidden
+    Na = T * k
+    D = (H + 4 * (H // 128)) if w.dispatch_dtype != "bf16" else 2 * H   # dispatched row incl. scales
+    return {
+        "route_topk": 4 * T * E + 8 * T * k,
+        "count": 8 * Na,
+        "scan": 8 * w.num_ranks * E,
+        "pack": 2 * H * T + Na * D,
+        "exchange": 2 * Na * D,
+        "stub": Na * D + Na * 2 * H,
+        "reverse_exchange": 2 * Na * 2 * H,
+        "reduce": Na * 2 * H + 2 * H * T,
+    }
+
+
+def metadata_bytes(w) -> int:
+    Na = w.tokens * w.top_k
+    # pack writes 16 B record + 4 B map per row and 8 B of positions per assignment;
+    # the exchange moves the record; the reverse exchange reads it
+    return Na * (16 + 4 + 8) + 2 * Na * 16 + Na * 16
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_router_softmax_expert_amd", "csrc")
+    for f in (KERNEL_SOURCES[kernel], "device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(config, {}).get(kernel)
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def cpu_baseline(w, inp, budget_s: float) -> dict:
+    """The oracle, as it stands, on one host core over a bounded sample of the workload."""
+    import numpy as np
+    from oracle import oracle as orc
+
+    # size the sample: whole workload if one pass fits the budget, else the first
+    # tokens of every rank (same ranks, experts, top-k and hidden size)
+    P, Tp = w.num_ranks, w.tokens_per_rank
+    probe_tp = max(1, min(Tp, 4))
+    old = os.sched_getaffinity(0)
+    core = min(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        def sub(tp):
+            sel = np.concatenate([np.arange(r * Tp, r * Tp + tp) for r in range(P)])
+            return orc.Shape(P, P * tp, w.num_experts, w.top_k, w.hidden, w.dispatch_dtype != "bf16"), \
+                np.ascontiguousarray(inp["x"][sel]), np.ascontiguousarray(inp["logits"][sel])
+
+        sh, x, lg = sub(probe_tp)
+        t0 = time.perf_counter()
+        orc.run(sh, x, lg)
+        per_token = (time.perf_counter() - t0) / sh.T
+        tp = int(min(Tp, max(1, budget_s / 3 / (per_token * P))))
+        sh, x, lg = sub(tp)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            orc.run(sh, x, lg)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    finally:
+        os.sched_setaffinity(0, old)
+    return {
+        "value": reps * sh.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{'whole workload' if tp == Tp else f'first {tp} of {Tp} tokens on each of {P} ranks'}"
+                   f" ({sh.T} tokens), route+dispatch+stub+combine, {reps} passes in {el:.1f} s, "
+                   f"single-threaded C oracle pinned to host core {core}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the expert-parallel ranks are emulated in one HBM "
+              "and nothing here uses a second GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_router_softmax_expert_amd import binding as B
+    from combine_router_softmax_expert_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.config]
+    inp = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ctx = B.Context.for_workload(w)
+    bufs = ctx.allocate(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.run_path(ctx, bufs, x, logits, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, every kernel bracketed by HIP events
+    B.moe_timing_begin(ctx)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    kt = B.moe_timing_end(ctx)
+    ms_per_step = total_ms / args.steps
+
+    # the same steps without the per-kernel events, for their overhead
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_no_events = ev0.elapsed_time(ev1) / args.steps
+
+    # per-step times with the caches flushed before each step (a 1 GiB write)
+    cold_ms = None
+    if not args.no_flush_run:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(min(args.steps, 30)):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        cold_ms = float(np.median(times))
+        del flush
+
+    kb = kernel_bytes(w)
+    per_kernel = {}
+    phases = {}
+    for name, (launches, tot) in kt.items():
+        avg = tot / launches
+        per_kernel[name] = {"launches": launches, "avg_us": round(avg * 1e3, 3),
+                            "algorithmic_bytes": kb[name],
+                            "gbps": round(kb[name] / (avg * 1e-3) / 1e9, 1)}
+        phases[PHASE_OF[name]] = phases.get(PHASE_OF[name], 0.0) + tot / args.steps
+    dom = max(kt, key=lambda n: kt[n][1])
+    dom_avg_s = kt[dom][1] / kt[dom][0] * 1e-3
+    achieved = kb[dom] / dom_avg_s / 1e9
+    traffic = load_traffic(args.config, dom)
+
+    T = w.tokens
+    dc_ms = phases.get("dispatch", 0.0) + phases.get("combine", 0.0)
+    dc_bytes = sum(kb[n] for n in ("count", "scan", "pack", "exchange", "reverse_exchange", "reduce"))
+    step_bytes = sum(kb.values())
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dispatch_dtype == "bf16" else "fp8_e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "ranks": w.num_ranks, "tokens": T, "experts": w.num_experts,
+                   "top_k": w.top_k, "hidden": w.hidden, "dispatch": w.dispatch_dtype,
+                   "parallelism": f"ep{w.num_ranks} emulated on 1 GPU"},
+        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "dispatch_combine": {
+            "ms": round(dc_ms, 5), "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
+            "algorithmic_bytes": dc_bytes, "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "phases_ms": {k: round(v, 5) for k, v in phases.items()},
+        "kernels": per_kernel,
+        "ms_per_step_without_kernel_events": round(ms_no_events, 5),
+        "ms_per_step_cache_flushed": None if cold_ms is None else round(cold_ms, 5),
+        "metadata_bytes_per_step": metadata_bytes(w),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

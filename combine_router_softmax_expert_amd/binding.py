@@ -1,0 +1,252 @@
+"""Thin ctypes binding of libmoe_ep.so (the C ABI in include/moe_ep.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (torch supplies device memory
+and streams); pointers and sizes go straight to the C calls.  If the library
+is missing this module raises on import: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_STALE_HANDLE = -4
+MOE_ERR_HIP = -5
+
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP8_E4M3 = 1
+
+FP8_BLOCK = 128
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("num_ranks", ctypes.c_int32), ("tokens_per_rank", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("dispatch_dtype", ctypes.c_int32)]
+
+
+class MoeMeta(ctypes.Structure):
+    _fields_ = [("src_rank", ctypes.c_int32), ("src_token", ctypes.c_int32), ("slot", ctypes.c_int16),
+                ("local_expert", ctypes.c_int16), ("weight", ctypes.c_float)]
+
+
+class MoeHandle(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_counts", "expert_offsets", "rank_recv_offsets", "count_matrix", "rank_expert_counts",
+        "send_offsets", "recv_offsets", "send_pos", "recv_pos", "send_meta", "recv_meta", "ctx")] + [
+        ("generation", ctypes.c_uint64)]
+
+
+class MoeKernelTime(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "moe_ctx_create": (I32, [ctypes.POINTER(MoeShape), ctypes.POINTER(P)]),
+        "moe_ctx_destroy": (None, [P]),
+        "moe_workspace_bytes": (SZ, [P]),
+        "moe_dispatch_row_bytes": (SZ, [P]),
+        "moe_scales_per_row": (I32, [P]),
+        "moe_num_assignments": (I64, [P]),
+        "moe_route_topk": (I32, [P, P, P, P, P]),
+        "moe_dispatch": (I32, [P, P, P, P, P, SZ, P, P, P, P, ctypes.POINTER(MoeHandle), P]),
+        "moe_expert_stub": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
+        "moe_combine": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
+        "moe_status_string": (ctypes.c_char_p, [I32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_timing_begin": (I32, [P]),
+        "moe_timing_end": (I32, [P, ctypes.POINTER(MoeKernelTime), I32, ctypes.POINTER(I32)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.moe_status_string(status).decode()
+        extra = lib.moe_last_error().decode() if status == MOE_ERR_HIP else ""
+        super().__init__(f"{where}: {msg}" + (f" ({extra})" if extra else ""))
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t, dtype=None, numel=None, name="tensor"):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() * t.element_size() < numel:
+        raise ValueError(f"{name} is too small: {t.numel() * t.element_size()} < {numel} bytes")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Context:
+    """Owns a moe_ctx (host object; no device memory)."""
+
+    def __init__(self, num_ranks: int, tokens_per_rank: int, num_experts: int, top_k: int, hidden: int,
+                 fp8: bool = False):
+        self.shape = MoeShape(num_ranks, tokens_per_rank, num_experts, top_k, hidden,
+                              MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16)
+        h = ctypes.c_void_p()
+        _check(lib.moe_ctx_create(ctypes.byref(self.shape), ctypes.byref(h)), "moe_ctx_create")
+        self._h = h
+        self.P, self.Tp, self.E, self.k, self.H, self.fp8 = num_ranks, tokens_per_rank, num_experts, top_k, hidden, fp8
+        self.T = num_ranks * tokens_per_rank
+
+    @classmethod
+    def for_workload(cls, w) -> "Context":
+        return cls(w.num_ranks, w.tokens_per_rank, w.num_experts, w.top_k, w.hidden, w.dispatch_dtype != "bf16")
+
+    @property
+    def handle_ptr(self):
+        return self._h
+
+    @property
+    def workspace_bytes(self) -> int:
+        return lib.moe_workspace_bytes(self._h)
+
+    @property
+    def row_bytes(self) -> int:
+        return lib.moe_dispatch_row_bytes(self._h)
+
+    @property
+    def scales_per_row(self) -> int:
+        return lib.moe_scales_per_row(self._h)
+
+    @property
+    def num_assignments(self) -> int:
+        return lib.moe_num_assignments(self._h)
+
+    def close(self):
+        if self._h:
+            lib.moe_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, device="cuda"):
+        """Caller-owned device buffers of the sizes the calls expect (torch.empty: contents undefined)."""
+        import torch
+        Na, H, T, k = self.num_assignments, self.H, self.T, self.k
+        nb = self.scales_per_row
+        b = {
+            "topk_ids": torch.empty((T, k), dtype=torch.int32, device=device),
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
+            "workspace": torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8, device=device),
+            "send": torch.empty((Na, self.row_bytes), dtype=torch.uint8, device=device),
+            "recv": torch.empty((Na, self.row_bytes), dtype=torch.uint8, device=device),
+            "send_scales": torch.empty((Na, nb), dtype=torch.float32, device=device) if self.fp8 else None,
+            "recv_scales": torch.empty((Na, nb), dtype=torch.float32, device=device) if self.fp8 else None,
+            "expert_out": torch.empty((Na, H), dtype=torch.bfloat16, device=device),
+            "comb": torch.empty((Na, H), dtype=torch.bfloat16, device=device),
+            "y": torch.empty((T, H), dtype=torch.bfloat16, device=device),
+        }
+        return b
+
+
+def moe_route_topk(ctx: Context, logits, topk_ids, topk_w, stream=None):
+    import torch
+    T, E, k = ctx.T, ctx.E, ctx.k
+    _check(lib.moe_route_topk(ctx.handle_ptr, _ptr(logits, torch.float32, 4 * T * E, "logits"),
+                              _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                              _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"), _stream(stream)),
+           "moe_route_topk")
+
+
+def moe_dispatch(ctx: Context, x, topk_ids, topk_w, workspace, send_buf, send_scales, recv_buf, recv_scales,
+                 stream=None) -> MoeHandle:
+    import torch
+    T, H, k, Na = ctx.T, ctx.H, ctx.k, ctx.num_assignments
+    rb, nb = ctx.row_bytes, ctx.scales_per_row
+    h = MoeHandle()
+    ws = _ptr(workspace, None, ctx.workspace_bytes, "workspace")
+    _check(lib.moe_dispatch(ctx.handle_ptr, _ptr(x, (torch.bfloat16, torch.int16), 2 * T * H, "x"),
+                            _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                            _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                            ws, workspace.numel() * workspace.element_size(),
+                            _ptr(send_buf, None, Na * rb, "send_buf"),
+                            _ptr(send_scales, torch.float32, 4 * Na * nb, "send_scales"),
+                            _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                            _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"),
+                            ctypes.byref(h), _stream(stream)), "moe_dispatch")
+    return h
+
+
+def moe_expert_stub(ctx: Context, handle: MoeHandle, recv_buf, recv_scales, expert_out, stream=None):
+    import torch
+    Na, H, rb, nb = ctx.num_assignments, ctx.H, ctx.row_bytes, ctx.scales_per_row
+    _check(lib.moe_expert_stub(ctx.handle_ptr, ctypes.byref(handle), _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                               _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"),
+                               _ptr(expert_out, (torch.bfloat16, torch.int16), 2 * Na * H, "expert_out"),
+                               _stream(stream)), "moe_expert_stub")
+
+
+def moe_combine(ctx: Context, handle: MoeHandle, expert_out, topk_w, comb_buf, y, stream=None):
+    import torch
+    Na, H, T, k = ctx.num_assignments, ctx.H, ctx.T, ctx.k
+    _check(lib.moe_combine(ctx.handle_ptr, ctypes.byref(handle),
+                           _ptr(expert_out, (torch.bfloat16, torch.int16), 2 * Na * H, "expert_out"),
+                           _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                           _ptr(comb_buf, (torch.bfloat16, torch.int16), 2 * Na * H, "comb_buf"),
+                           _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
+           "moe_combine")
+
+
+def moe_timing_begin(ctx: Context):
+    _check(lib.moe_timing_begin(ctx.handle_ptr), "moe_timing_begin")
+
+
+def moe_timing_end(ctx: Context) -> dict:
+    recs = (MoeKernelTime * 64)()
+    n = ctypes.c_int32()
+    _check(lib.moe_timing_end(ctx.handle_ptr, recs, 64, ctypes.byref(n)), "moe_timing_end")
+    return {recs[i].kernel.decode(): (recs[i].launches, recs[i].total_ms) for i in range(min(n.value, 64))}
+
+
+def run_path(ctx: Context, bufs: dict, x, logits, stream=None) -> MoeHandle:
+    """One pass of the whole path: route, dispatch, expert stub, combine."""
+    moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"], stream)
+    h = moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                     bufs["send_scales"], bufs["recv"], bufs["recv_scales"], stream)
+    moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"], stream)
+    moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+    return h

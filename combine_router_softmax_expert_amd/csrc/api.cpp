@@ -1,0 +1,313 @@
+// api.cpp -- the C ABI of libmoe_ep.so (declared in include/moe_ep.h): argument
+// validation, workspace layout, launch sequencing on the caller's stream, the
+// handle's generation check and optional per-kernel event timing.
+#include "moe_ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+constexpr int kFp8Block = 128;   // channels per FP8 scale, per token
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct TimingRecord {
+    const char* name;
+    hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct moe_ctx {
+    moe_shape shape;
+    moe::Dims d;
+    // byte offsets of the workspace arrays
+    size_t o_n, o_N, o_expert_off, o_rank_recv_off, o_send_off, o_recv_off, o_C, o_bucket_rank, o_send_pos,
+        o_recv_pos, o_send_to_recv, o_send_meta, o_recv_meta, ws_bytes;
+    uint64_t generation = 0;
+    bool timing = false;
+    std::vector<TimingRecord> records;
+    std::vector<hipEvent_t> free_events;
+};
+
+namespace {
+
+moe_status hip_fail(hipError_t e, const char* where) {
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return MOE_ERR_HIP;
+}
+
+hipEvent_t take_event(moe_ctx* ctx) {
+    if (!ctx->free_events.empty()) {
+        hipEvent_t e = ctx->free_events.back();
+        ctx->free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launches one kernel through `fn`, bracketed by events when timing is on.
+template <typename Fn>
+moe_status launch(moe_ctx* ctx, const char* name, hipStream_t st, Fn&& fn) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (ctx->timing) {
+        a = take_event(ctx);
+        b = take_event(ctx);
+        if (!a || !b) return hip_fail(hipErrorOutOfMemory, "hipEventCreate");
+        hipError_t e = hipEventRecord(a, st);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    hipError_t e = fn();
+    if (e != hipSuccess) return hip_fail(e, name);
+    if (ctx->timing) {
+        e = hipEventRecord(b, st);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        ctx->records.push_back({name, a, b});
+    }
+    return MOE_OK;
+}
+
+moe::Workspace carve(const moe_ctx* ctx, void* base) {
+    char* p = static_cast<char*>(base);
+    moe::Workspace w;
+    w.n = reinterpret_cast<int32_t*>(p + ctx->o_n);
+    w.N = reinterpret_cast<int32_t*>(p + ctx->o_N);
+    w.expert_off = reinterpret_cast<int32_t*>(p + ctx->o_expert_off);
+    w.rank_recv_off = reinterpret_cast<int32_t*>(p + ctx->o_rank_recv_off);
+    w.send_off = reinterpret_cast<int32_t*>(p + ctx->o_send_off);
+    w.recv_off = reinterpret_cast<int32_t*>(p + ctx->o_recv_off);
+    w.C = reinterpret_cast<int32_t*>(p + ctx->o_C);
+    w.bucket_rank = reinterpret_cast<int32_t*>(p + ctx->o_bucket_rank);
+    w.send_pos = reinterpret_cast<int32_t*>(p + ctx->o_send_pos);
+    w.recv_pos = reinterpret_cast<int32_t*>(p + ctx->o_recv_pos);
+    w.send_to_recv = reinterpret_cast<int32_t*>(p + ctx->o_send_to_recv);
+    w.send_meta = p + ctx->o_send_meta;
+    w.recv_meta = p + ctx->o_recv_meta;
+    return w;
+}
+
+// The arrays the expert stage and the combine read, taken from the handle.
+moe::Workspace from_handle(const moe_handle* h) {
+    moe::Workspace w{};
+    w.rank_recv_off = const_cast<int32_t*>(h->rank_recv_offsets);
+    w.recv_meta = const_cast<moe_meta*>(h->recv_meta);
+    return w;
+}
+
+moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
+    if (!h) return MOE_ERR_INVALID_ARG;
+    if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0) return MOE_ERR_STALE_HANDLE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_STALE_HANDLE: return "stale or foreign dispatch handle";
+        case MOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!shape) return MOE_ERR_INVALID_ARG;
+    const moe_shape s = *shape;
+    if (s.num_ranks < 1 || s.tokens_per_rank < 0 || s.num_experts < 1 || s.top_k < 1 || s.hidden < 8 ||
+        s.num_experts % s.num_ranks != 0 || s.top_k > s.num_experts || s.hidden % 8 != 0 ||
+        (s.dispatch_dtype != MOE_DTYPE_BF16 && s.dispatch_dtype != MOE_DTYPE_FP8_E4M3))
+        return MOE_ERR_INVALID_ARG;
+    const bool fp8 = s.dispatch_dtype == MOE_DTYPE_FP8_E4M3;
+    const long long T = (long long)s.num_ranks * s.tokens_per_rank;
+    const long long Na = T * s.top_k;
+    if (s.num_experts > 1024 || s.num_experts / s.num_ranks > 32767 || s.top_k > 32 || s.hidden > 65536 ||
+        (fp8 && s.hidden % kFp8Block != 0) || Na >= (1LL << 31) ||
+        Na * (s.hidden / 1024 + 1) >= (1LL << 31))
+        return MOE_ERR_UNSUPPORTED;
+
+    moe_ctx* ctx = new (std::nothrow) moe_ctx();
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    ctx->shape = s;
+    moe::Dims& d = ctx->d;
+    d.P = s.num_ranks;
+    d.Tp = s.tokens_per_rank;
+    d.T = (int)T;
+    d.E = s.num_experts;
+    d.Ep = s.num_experts / s.num_ranks;
+    d.k = s.top_k;
+    d.H = s.hidden;
+    d.fp8 = fp8;
+    d.Na = Na;
+    d.row_units = fp8 ? s.hidden / 16 : s.hidden / 8;
+    d.out_units = s.hidden / 8;
+    d.scales = fp8 ? s.hidden / kFp8Block : 0;
+
+    const size_t P = d.P, E = d.E, tk = (size_t)Na;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    ctx->o_n = take(4 * P * E);
+    ctx->o_N = take(4 * E);
+    ctx->o_expert_off = take(4 * (E + 1));
+    ctx->o_rank_recv_off = take(4 * (P + 1));
+    ctx->o_send_off = take(4 * P * E);
+    ctx->o_recv_off = take(4 * E * P);
+    ctx->o_C = take(4 * P * P);
+    ctx->o_bucket_rank = take(4 * tk);
+    ctx->o_send_pos = take(4 * tk);
+    ctx->o_recv_pos = take(4 * tk);
+    ctx->o_send_to_recv = take(4 * tk);
+    ctx->o_send_meta = take(sizeof(moe_meta) * tk);
+    ctx->o_recv_meta = take(sizeof(moe_meta) * tk);
+    ctx->ws_bytes = off;
+    *out = ctx;
+    return MOE_OK;
+}
+
+void moe_ctx_destroy(moe_ctx* ctx) {
+    if (!ctx) return;
+    for (auto& r : ctx->records) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    for (auto e : ctx->free_events) (void)hipEventDestroy(e);
+    delete ctx;
+}
+
+size_t moe_workspace_bytes(const moe_ctx* ctx) { return ctx ? ctx->ws_bytes : 0; }
+size_t moe_dispatch_row_bytes(const moe_ctx* ctx) { return ctx ? (size_t)ctx->d.row_units * 16 : 0; }
+int32_t moe_scales_per_row(const moe_ctx* ctx) { return ctx ? ctx->d.scales : 0; }
+int64_t moe_num_assignments(const moe_ctx* ctx) { return ctx ? ctx->d.Na : 0; }
+
+moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    if (ctx->d.T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const moe::Dims d = ctx->d;
+    return launch(ctx, "route_topk", st, [&] { return moe::launch_route_topk(d, logits, topk_ids, topk_w, st); });
+}
+
+moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
+                        void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const moe::Dims d = ctx->d;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
+        return MOE_ERR_INVALID_ARG;
+
+    const moe::Workspace ws = carve(ctx, workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    moe_status s = MOE_OK;
+    if (d.T > 0) {
+        s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
+        if (s == MOE_OK) s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        if (s == MOE_OK)
+            s = launch(ctx, "pack", st, [&] {
+                return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, st);
+            });
+        if (s == MOE_OK)
+            s = launch(ctx, "exchange", st, [&] {
+                return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, st);
+            });
+        if (s != MOE_OK) return s;
+    }
+    ctx->generation += 1;
+    handle->expert_counts = ws.N;
+    handle->expert_offsets = ws.expert_off;
+    handle->rank_recv_offsets = ws.rank_recv_off;
+    handle->count_matrix = ws.C;
+    handle->rank_expert_counts = ws.n;
+    handle->send_offsets = ws.send_off;
+    handle->recv_offsets = ws.recv_off;
+    handle->send_pos = ws.send_pos;
+    handle->recv_pos = ws.recv_pos;
+    handle->send_meta = static_cast<const moe_meta*>(ws.send_meta);
+    handle->recv_meta = static_cast<const moe_meta*>(ws.recv_meta);
+    handle->ctx = ctx;
+    handle->generation = ctx->generation;
+    return MOE_OK;
+}
+
+moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf, const float* recv_scales,
+                           uint16_t* expert_out, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_handle(ctx, handle);
+    if (s != MOE_OK) return s;
+    const moe::Dims d = ctx->d;
+    if (d.T == 0) return MOE_OK;
+    if (!recv_buf || !expert_out || (d.fp8 ? !recv_scales : recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    const moe::Workspace ws = from_handle(handle);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch(ctx, "stub", st, [&] { return moe::launch_stub(d, ws, recv_buf, recv_scales, expert_out, st); });
+}
+
+moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out, const float* topk_w,
+                       uint16_t* comb_buf, uint16_t* y, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_handle(ctx, handle);
+    if (s != MOE_OK) return s;
+    const moe::Dims d = ctx->d;
+    if (d.T == 0) return MOE_OK;
+    if (!expert_out || !topk_w || !comb_buf || !y) return MOE_ERR_INVALID_ARG;
+    const moe::Workspace ws = from_handle(handle);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    s = launch(ctx, "reverse_exchange", st, [&] { return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, st); });
+    if (s != MOE_OK) return s;
+    return launch(ctx, "reduce", st, [&] { return moe::launch_reduce(d, comb_buf, topk_w, y, st); });
+}
+
+moe_status moe_timing_begin(moe_ctx* ctx) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    ctx->timing = true;
+    return MOE_OK;
+}
+
+moe_status moe_timing_end(moe_ctx* ctx, moe_kernel_time* out, int32_t max, int32_t* count) {
+    if (!ctx || !count || (max > 0 && !out)) return MOE_ERR_INVALID_ARG;
+    ctx->timing = false;
+    std::vector<moe_kernel_time> agg;
+    moe_status status = MOE_OK;
+    for (auto& r : ctx->records) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess && status == MOE_OK) status = hip_fail(e, "hipEventElapsedTime");
+        size_t i = 0;
+        while (i < agg.size() && std::strcmp(agg[i].kernel, r.name) != 0) ++i;
+        if (i == agg.size()) agg.push_back({r.name, 0, 0.0f});
+        agg[i].launches += 1;
+        agg[i].total_ms += ms;
+        ctx->free_events.push_back(r.start);
+        ctx->free_events.push_back(r.stop);
+    }
+    ctx->records.clear();
+    *count = (int32_t)agg.size();
+    for (int32_t i = 0; i < (int32_t)agg.size() && i < max; ++i) out[i] = agg[i];
+    return status;
+}
+
+}  // extern "C"

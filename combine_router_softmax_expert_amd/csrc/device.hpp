@@ -1,0 +1,106 @@
+// device.hpp -- gfx950 device helpers shared by the dispatch/combine kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kFp8Block = 128;   // channels per FP8 scale, per token
+
+// ---- bfloat16 ------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Two fp32 values -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950),
+// `lo` in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 8 bf16 in a 16-byte vector -> 8 fp32
+__device__ __forceinline__ void unpack8_bf16(const uint4& v, float (&f)[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
+    uint4 v;
+    v.x = pack_bf16x2(f[0], f[1]);
+    v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]);
+    v.w = pack_bf16x2(f[6], f[7]);
+    return v;
+}
+
+// ---- OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 significand bits,
+// largest finite 448, NaN = S.1111.111, no infinities) ------------------------------
+
+// Nearest code to a finite fp32 value, ties to the even code, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x43E00000u) return sign | 0x7Eu;          // |f| >= 448 (also inf)
+    if (a < 0x3C800000u) {                              // |f| < 2^-6: subnormal codes m * 2^-9
+        // |f| * 512 is exact; round to the nearest integer 0..8 (8 is the smallest normal code)
+        const float r = __builtin_rintf(__uint_as_float(a) * 512.0f);
+        return sign | (uint32_t)r;
+    }
+    // normal: keep 3 of the 23 fraction bits, round the other 20 to nearest even;
+    // a carry out of the fraction moves to the next exponent, as the code layout intends
+    const uint32_t exp = (a >> 23) - 120u;              // rebias 127 -> 7
+    uint32_t code = (exp << 3) | ((a >> 20) & 7u);
+    const uint32_t rest = a & 0xFFFFFu;
+    code += (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) ? 1u : 0u;
+    return sign | code;                                  // |f| < 448 keeps code <= 0x7E
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 0x1p-9f));
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// ---- wave helpers ---------------------------------------------------------------
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
+// `tmp` needs blockDim.x / 64 + 1 ints of LDS.  Every thread of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < nw ? tmp[lane] : 0;
+        const int wincl = wave_inclusive_scan(w);
+        if (lane < nw) tmp[lane] = wincl - w;
+        if (lane == nw - 1) tmp[nw] = wincl;
+    }
+    __syncthreads();
+    const int out = tmp[wave] + incl - v;
+    if (total) *total = tmp[nw];
+    __syncthreads();
+    return out;
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+// kernels.hpp -- host launchers of the gfx950 kernels (internal to libmoe_ep.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Dims {
+    int P, Tp, T, E, Ep, k, H;
+    bool fp8;
+    long long Na;          // T * k
+    int row_units;         // 16-byte units per dispatched row (2H/16 or H/16)
+    int out_units;         // 16-byte units per bf16 output row (2H/16)
+    int scales;            // fp32 scales per dispatched row (H/128 or 0)
+};
+
+struct Workspace {         // device arrays carved from the caller's workspace
+    int32_t* n;            // [P][E]
+    int32_t* N;            // [E]
+    int32_t* expert_off;   // [E+1]
+    int32_t* rank_recv_off;// [P+1]
+    int32_t* send_off;     // [P][E]
+    int32_t* recv_off;     // [E][P]
+    int32_t* C;            // [P][P]
+    int32_t* bucket_rank;  // [T*k] rank of the assignment inside its (source, expert) bucket
+    int32_t* send_pos;     // [T*k]
+    int32_t* recv_pos;     // [T*k]
+    int32_t* send_to_recv; // [N_a]
+    void* send_meta;       // [N_a] 16-byte records
+    void* recv_meta;       // [N_a]
+};
+
+hipError_t launch_route_topk(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, hipStream_t st);
+hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st);
+hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w,
+                       const Workspace& ws, void* send, float* send_scales, hipStream_t st);
+hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
+                           void* recv, float* recv_scales, hipStream_t st);
+hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales,
+                       uint16_t* out, hipStream_t st);
+hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out,
+                                   uint16_t* comb, hipStream_t st);
+hipError_t launch_reduce(const Dims& d, const uint16_t* comb, const float* w, uint16_t* y, hipStream_t st);
+
+// Threads per block for a row of `n` per-thread work items: the whole row when it
+// fits in 512 threads, else a divisor of n from 512 down to 256, else 256.
+inline int pick_block(long long n) {
+    if (n <= 512) return (int)((n + 63) / 64 * 64);
+    for (int b = 512; b >= 256; b -= 64)
+        if (n % b == 0) return b;
+    return 256;
+}
+
+// LDS bytes / words-per-expert choice of the count kernel (shared with the host checks)
+int count_words_per_expert(int E, int Tp);
+size_t count_lds_bytes(int E, int W);
+
+}  // namespace moe

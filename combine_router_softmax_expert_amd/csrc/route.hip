@@ -1,0 +1,110 @@
+// route.hip -- router softmax + top-k + renormalised weights on gfx950.
+//
+// Follows the router paragraph of "高效且便携的专家混合通信" (pplx-kernels): the
+// router's probability distribution over experts, the top-k experts, and
+// weights taken from that distribution; "Expert Parallel: MoE Token ..."
+// section "Dispatch 前为什么必须 count 和 permute" fixes the output as
+// [num_tokens, top_k] ids and weights.
+//
+// A group of G lanes of one wavefront owns a token (G = 64 for E > 32, else the
+// next power of two >= E, so small-E routers put 64/G tokens in a wave).  Each
+// lane holds V = ceil(E / G) logits, loaded with the group's lanes on
+// consecutive addresses.  Top-k is k rounds of a group arg-max over 64-bit keys
+// (order-preserving logit bits, then the complemented expert id, so that equal
+// logits pick the lower id) by xor-butterfly shuffles; the winner's lane drops
+// it.  Softmax is strictly increasing, so selecting by logit is selecting by
+// probability, and the renormalised weight p_j / sum_sel p equals
+// exp(l_j - l_max) / sum_sel exp(l_i - l_max): the full partition function
+// cancels.  Those k exponentials and the slot-order sum run in double, so the
+// fp32 weights are the correctly rounded ones up to a double ulp.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 ranks equal to +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int G, int V>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w, int T, int E, int k) {
+    constexpr int kTokensPerWave = kWave / G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gl = lane % G;
+    const int wave = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int t = wave * kTokensPerWave + lane / G;
+    const bool valid = t < T;
+
+    uint64_t key[V];
+    const float* row = logits + (size_t)(valid ? t : 0) * E;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = gl + G * v;
+        key[v] = 0;   // below every real key
+        if (valid && e < E) key[v] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)~(uint32_t)e;
+    }
+
+    double m = 0.0, sum = 0.0, my_e = 0.0;
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) {
+            const uint64_t o = __shfl_xor(best, off, G);
+            best = o > best ? o : best;
+        }
+        const int id = (int)~(uint32_t)best;
+        const double lv = (double)from_ordered_bits((uint32_t)(best >> 32));
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (gl + G * v == id) key[v] = 0;
+        if (j == 0) m = lv;
+        const double ej = exp(lv - m);
+        sum += ej;                       // slot order
+        if (gl == j) { my_id = id; my_e = ej; }
+    }
+    if (valid && gl < k) {
+        ids[(size_t)t * k + gl] = my_id;
+        w[(size_t)t * k + gl] = (float)(my_e / sum);
+    }
+}
+
+template <int G, int V>
+hipError_t launch_rt(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st) {
+    constexpr int kThreads = 256;
+    const int tokens_per_block = (kThreads / kWave) * (kWave / G);
+    const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
+    hipLaunchKernelGGL((route_topk_kernel<G, V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w,
+                       d.T, d.E, d.k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st) {
+    if (d.T == 0) return hipSuccess;
+    const int E = d.E;
+    if (E <= 1) return launch_rt<1, 1>(d, logits, ids, w, st);
+    if (E <= 2) return launch_rt<2, 1>(d, logits, ids, w, st);
+    if (E <= 4) return launch_rt<4, 1>(d, logits, ids, w, st);
+    if (E <= 8) return launch_rt<8, 1>(d, logits, ids, w, st);
+    if (E <= 16) return launch_rt<16, 1>(d, logits, ids, w, st);
+    if (E <= 32) return launch_rt<32, 1>(d, logits, ids, w, st);
+    if (E <= 64) return launch_rt<64, 1>(d, logits, ids, w, st);
+    if (E <= 128) return launch_rt<64, 2>(d, logits, ids, w, st);
+    if (E <= 256) return launch_rt<64, 4>(d, logits, ids, w, st);
+    if (E <= 512) return launch_rt<64, 8>(d, logits, ids, w, st);
+    return launch_rt<64, 16>(d, logits, ids, w, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,89 @@
+// stub.hip -- per-expert scalar stand-in for the grouped GEMM that consumes the
+// expert-contiguous receive rows ("[Infra-10] All-to-All Optimization" 5.2:
+// the receive layout is the expert kernel's input; "Expert Parallel: MoE Token
+// ..." worked example: each rank runs its local experts on what it received).
+//
+// expert_out[q] = bf16(deq(recv[q]) * m_e), m_e = (E + e) / E in fp32, with e
+// the global expert of receive row q: local expert from the row's handle record
+// and owner rank from the receive-region offsets (a wave ballot over
+// rank_recv_off).  deq is the bf16 value itself, or code * scale in fp32 for
+// e4m3 rows (lane = 16 codes of one 128-channel block).  Each product rounds
+// to fp32 and the result once to bf16.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+struct Rec { int32_t src_rank, src_token; int16_t slot, local_expert; float weight; };
+
+// Rank whose receive region holds row q: the number of region starts <= q, less one.
+__device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_off, int P, int q) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int count = 0;
+    for (int r0 = 0; r0 <= P; r0 += kWave) {
+        const int r = r0 + lane;
+        const bool le = r <= P && rank_recv_off[r] <= q;
+        count += __popcll(__ballot(le));
+    }
+    return count - 1;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
+                                                   const Rec* __restrict__ meta,
+                                                   const int32_t* __restrict__ rank_recv_off,
+                                                   uint4* __restrict__ out, int P, int E, int Ep, int L,
+                                                   int slices) {
+    const int q = blockIdx.x / slices;
+    const int slice = blockIdx.x - q * slices;
+    const int r = owner_rank(rank_recv_off, P, q);
+    const int e = r * Ep + meta[q].local_expert;
+    const float m = (float)(E + e) / (float)E;
+    const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
+    if (u >= L) return;
+    if (FP8) {
+        const uint4 c = recv[(size_t)q * L + u];
+        const float sc = scales[(size_t)q * (L / 8) + (u >> 3)];
+        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float d = e4m3_to_f32((words[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
+            f[i] = d * m;
+        }
+        float lo[8], hi[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { lo[i] = f[i]; hi[i] = f[8 + i]; }
+        out[(size_t)q * (2 * L) + 2 * u] = pack8_bf16(lo);
+        out[(size_t)q * (2 * L) + 2 * u + 1] = pack8_bf16(hi);
+    } else {
+        float f[8];
+        unpack8_bf16(recv[(size_t)q * L + u], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = f[i] * m;
+        out[(size_t)q * L + u] = pack8_bf16(f);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales, uint16_t* out,
+                       hipStream_t st) {
+    if (d.Na == 0) return hipSuccess;
+    const int L = d.row_units;
+    const int B = pick_block(L);
+    const int slices = (L + B - 1) / B;
+    const dim3 grid((unsigned)(d.Na * slices));
+    if (d.fp8)
+        hipLaunchKernelGGL(stub_kernel<true>, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+                           reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off,
+                           reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, slices);
+    else
+        hipLaunchKernelGGL(stub_kernel<false>, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+                           reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off,
+                           reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, slices);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -100,30 +100,50 @@ def stream_seed(seed: int, stream: int) -> int:
     return int(splitmix64(seed, stream, 1)[0])
 
 
-def uniforms(seed: int, start: int, count: int) -> np.ndarray:
-    z = splitmix64(seed, start, count)
-    return ((z >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+def _i64(v: int) -> int:
+    """The int64 with the same 64 bits as the unsigned value v."""
+    v &= 0xFFFFFFFFFFFFFFFF
+    return v - (1 << 64) if v >= (1 << 63) else v
 
 
-def normals(seed: int, count: int, chunk: int = 1 << 23) -> np.ndarray:
+def _splitmix64_torch(seed: int, start: int, count: int):
+    """Same outputs as ``splitmix64`` as int64 bit patterns, on torch's multithreaded CPU ops
+    (wrapping int64 products keep the low 64 bits; logical shifts are arithmetic shifts
+    masked to the bits a logical shift keeps)."""
+    import torch
+    idx = torch.arange(start + 1, start + count + 1, dtype=torch.int64)
+    z = idx * _i64(int(GOLDEN)) + _i64(seed)
+    for sh, mul in ((30, _i64(int(_M1))), (27, _i64(int(_M2))), (31, None)):
+        z = z ^ ((z >> sh) & ((1 << (64 - sh)) - 1))
+        if mul is not None:
+            z = z * mul
+    return z
+
+
+def normals(seed: int, count: int, chunk: int = 1 << 24) -> np.ndarray:
     """``count`` standard normals (float64) by Box-Muller over consecutive uniform pairs."""
+    import torch
     out = np.empty(count, dtype=np.float64)
     pairs = (count + 1) // 2
     done = 0
     while done < pairs:
         m = min(chunk, pairs - done)
-        u = uniforms(seed, 2 * done, 2 * m).reshape(m, 2)
-        r = np.sqrt(-2.0 * np.log(u[:, 0]))
-        th = 2.0 * np.pi * u[:, 1]
-        z = np.empty((m, 2), dtype=np.float64)
-        z[:, 0] = r * np.cos(th)
-        z[:, 1] = r * np.sin(th)
-        flat = z.reshape(-1)
+        z = _splitmix64_torch(seed, 2 * done, 2 * m)
+        u = (((z >> 11) & ((1 << 53) - 1)).to(torch.float64) + 1.0) * (2.0 ** -53)
+        u = u.view(m, 2)
+        r = torch.sqrt(-2.0 * torch.log(u[:, 0]))
+        th = (2.0 * np.pi) * u[:, 1]
+        zz = torch.stack((r * torch.cos(th), r * torch.sin(th)), dim=1).reshape(-1).numpy()
         lo = 2 * done
         hi = min(count, lo + 2 * m)
-        out[lo:hi] = flat[: hi - lo]
+        out[lo:hi] = zz[: hi - lo]
         done += m
     return out
+
+
+def uniforms(seed: int, start: int, count: int) -> np.ndarray:
+    z = splitmix64(seed, start, count)
+    return ((z >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
 
 
 def float32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -148,8 +168,9 @@ def expert_bias(seed: int, num_experts: int) -> np.ndarray:
 
 def make_hidden(seed: int, tokens: int, hidden: int) -> np.ndarray:
     """bfloat16 hidden states ``[tokens, hidden]`` ~ N(0, 1), as uint16 bit patterns."""
-    z = normals(stream_seed(seed, STREAM_X), tokens * hidden).astype(np.float32)
-    return float32_to_bf16_bits(z).reshape(tokens, hidden)
+    import torch
+    z = torch.from_numpy(normals(stream_seed(seed, STREAM_X), tokens * hidden)).to(torch.float32)
+    return z.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).reshape(tokens, hidden)
 
 
 def make_logits(seed: int, tokens: int, num_experts: int, zipf: bool = False) -> np.ndarray:

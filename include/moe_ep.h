@@ -1,0 +1,219 @@
+/*
+ * moe_ep.h -- C ABI of the MI355X (gfx950) expert-parallel dispatch/combine
+ * library libmoe_ep.so.
+ *
+ * The path, for P logical expert-parallel ranks emulated in one GPU's HBM:
+ *   moe_route_topk   router softmax + top-k + renormalised weights
+ *   moe_dispatch     count, prefix sums, stable permute-and-pack of the hidden
+ *                    rows plus a combine handle into all-to-all-v send
+ *                    buffers, then the exchange into the receive buffers
+ *   moe_expert_stub  a per-expert scalar stand-in for the grouped GEMM
+ *   moe_combine      reverse exchange, then the routing-weighted top-k
+ *                    reduction back into original token order
+ *
+ * Sources (web pages on expert-parallel all-to-all; cited by title and section):
+ *  [EP]   "Expert Parallel: MoE Token 为什么要两次穿过 GPU 网络" (charlestar.github.io)
+ *  [A2A]  "[Infra-10] All-to-All Optimization" (xutianle.me)
+ *  [PPLX] "高效且便携的专家混合通信" (Perplexity's pplx-kernels article)
+ *
+ * Conventions for every call:
+ *  - Shapes: P = num_ranks, T/P = tokens_per_rank (token t lives on rank
+ *    s = t / (T/P), local index i = t mod (T/P)), E = num_experts (expert e is
+ *    owned by rank e / (E/P)), k = top_k, H = hidden, N_a = T * k assignments.
+ *  - Every data pointer is a DEVICE pointer into caller-owned memory on the
+ *    current HIP device; ctx, shape, handle and status outputs are HOST
+ *    pointers.  `stream` is a hipStream_t (NULL = default stream).
+ *  - Calls only enqueue work on `stream`: they never allocate device memory,
+ *    never synchronise and never read device data on the host ([A2A] 3.5: a
+ *    count read back to the CPU puts a hole before the exchange; [EP]
+ *    "显存账不只有 expert 权重": buffers are preallocated at the maximum size).
+ *  - Host-detectable errors are returned synchronously and nothing is
+ *    enqueued; launch failures return MOE_ERR_HIP.  Expert ids outside
+ *    [0, E) or repeated within a token are outside the contract.
+ *  - T = 0 is a valid no-op.  No C++ exception crosses this ABI.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size or shape */
+    MOE_ERR_UNSUPPORTED = -2,   /* shape outside the supported limits below */
+    MOE_ERR_WORKSPACE = -3,     /* workspace smaller than moe_workspace_bytes() */
+    MOE_ERR_STALE_HANDLE = -4,  /* handle not from the latest moe_dispatch of this ctx */
+    MOE_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum {
+    MOE_DTYPE_BF16 = 0,         /* rows of H bfloat16 values (2H bytes) */
+    MOE_DTYPE_FP8_E4M3 = 1      /* rows of H OCP E4M3 codes + H/128 fp32 scales */
+} moe_dtype;
+
+/* Problem shape.  Limits: 1 <= P; E % P == 0; E <= 1024; E/P <= 32767;
+ * 1 <= k <= min(E, 32); H % 8 == 0 and 8 <= H; FP8 needs H % 128 == 0;
+ * T * k < 2^31. */
+typedef struct {
+    int32_t num_ranks;
+    int32_t tokens_per_rank;
+    int32_t num_experts;
+    int32_t top_k;
+    int32_t hidden;
+    int32_t dispatch_dtype;     /* moe_dtype */
+} moe_shape;
+
+/* The 16-byte record that travels with every dispatched row ([EP] "dispatch
+ * payload": local expert id, source token index, top-k slot and routing
+ * weight; [EP] "combine handle": source rank and token, top-k slot, weight;
+ * [PPLX] dispatch-receive stores source rank, expert and token index for the
+ * combine). */
+typedef struct {
+    int32_t src_rank;           /* s */
+    int32_t src_token;          /* i, index local to rank s */
+    int16_t slot;               /* j, top-k slot of the assignment */
+    int16_t local_expert;       /* e mod (E/P) */
+    float weight;               /* topk_w[t, j] */
+} moe_meta;
+
+/* Opaque host-side context: shape, workspace layout, handle generation.  It
+ * owns no device memory. */
+typedef struct moe_ctx moe_ctx;
+
+/* What moe_dispatch returns for the combine and for the expert stage ([EP]
+ * "Combine 不是简单把结果发回来": dispatch hands the combine a handle that
+ * holds the buffer positions, source rank and token, top-k slot, per-expert
+ * counts and the weight, and exposes each local expert's received count for
+ * the grouped GEMM shape).  All arrays are device pointers into the caller's
+ * workspace, valid until the next moe_dispatch on the same ctx. */
+typedef struct {
+    const int32_t* expert_counts;       /* [E]     N[e], rows received by expert e */
+    const int32_t* expert_offsets;      /* [E+1]   first receive row of expert e */
+    const int32_t* rank_recv_offsets;   /* [P+1]   first receive row of rank r */
+    const int32_t* count_matrix;        /* [P][P]  C[s][r], rows sent from s to r */
+    const int32_t* rank_expert_counts;  /* [P][E]  n[s][e] */
+    const int32_t* send_offsets;        /* [P][E]  first send row of bucket (s -> e) */
+    const int32_t* recv_offsets;        /* [E][P]  first receive row of bucket (s -> e) */
+    const int32_t* send_pos;            /* [T][k]  send row of assignment (t, j) */
+    const int32_t* recv_pos;            /* [T][k]  receive row of assignment (t, j) */
+    const moe_meta* send_meta;          /* [N_a]   record of each send row */
+    const moe_meta* recv_meta;          /* [N_a]   record of each receive row */
+    const void* ctx;                    /* the ctx that issued it */
+    uint64_t generation;                /* dispatch sequence number on that ctx */
+} moe_handle;
+
+/* Per-kernel timing record (moe_timing_end). */
+typedef struct {
+    const char* kernel;         /* static name of the kernel */
+    int32_t launches;
+    float total_ms;             /* sum of HIP-event durations of its launches */
+} moe_kernel_time;
+
+/* ---- context and sizes ---------------------------------------------------- */
+
+/* Validates the shape and creates a context.  Returns MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED (and *out = NULL) for shapes outside the limits. */
+moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out);
+void moe_ctx_destroy(moe_ctx* ctx);
+
+/* Device workspace moe_dispatch needs (counts, offsets, positions, the send
+ * and receive handle records).  0 for a NULL ctx. */
+size_t moe_workspace_bytes(const moe_ctx* ctx);
+/* Bytes of one dispatched row: 2H (bf16) or H (e4m3).  0 for a NULL ctx. */
+size_t moe_dispatch_row_bytes(const moe_ctx* ctx);
+/* fp32 scales per dispatched row: H/128 for e4m3, 0 for bf16. */
+int32_t moe_scales_per_row(const moe_ctx* ctx);
+/* N_a = T * k, the rows of every send, receive, expert-output and combine buffer. */
+int64_t moe_num_assignments(const moe_ctx* ctx);
+
+/* ---- the path ------------------------------------------------------------- */
+
+/* Router ([PPLX] router paragraph: a small linear layer yields a probability
+ * distribution over experts, the top-k experts are taken and their outputs
+ * are averaged with the router's weights; [EP] "Dispatch 前为什么必须 count 和
+ * permute": the router output is [num_tokens, top_k] expert ids and weights).
+ *   logits   fp32 [T][E], row-major
+ *   topk_ids int32 [T][k] out: slot j holds the expert with the j-th largest
+ *            probability (softmax is strictly increasing, so: the j-th largest
+ *            logit); equal logits are ordered by lower expert id
+ *   topk_w   fp32 [T][k] out: p_e / sum of p over the k chosen experts, with
+ *            p = softmax(logits row) (computed in double, rounded to fp32)
+ * Error: MOE_ERR_INVALID_ARG on a NULL ctx or (T > 0) a NULL array. */
+moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, float* topk_w,
+                          void* stream);
+
+/* Dispatch ([EP] sections "Dispatch 前为什么必须 count 和 permute" and
+ * "All-to-All-v 才接近真实通信形状"; [A2A] 3.5 count / prefix sum / scatter /
+ * pack, 4.3 and 5.1 write the permutation straight into the communication
+ * buffer, 5.2 destination-contiguous send layout bucketed by local expert;
+ * [A2A] 1 all-to-all as a distributed transpose).
+ *   x            bf16 [T][H] hidden states (uint16 bit patterns)
+ *   topk_ids     int32 [T][k], topk_w fp32 [T][k] (from moe_route_topk or the caller)
+ *   workspace    device scratch of >= moe_workspace_bytes() bytes, 256-byte aligned
+ *   send_buf     [N_a][row] out: rank s owns rows [s*(T/P)*k, (s+1)*(T/P)*k),
+ *                ordered by destination rank, then local expert, then token
+ *   send_scales  fp32 [N_a][H/128] out (e4m3 only, else NULL): per token and
+ *                128-channel block, scale = amax / 448 and code = e4m3(x / scale)
+ *                (fp32 division, round to nearest even, saturating)
+ *   recv_buf     [N_a][row] out: rank r's region is contiguous; inside it rows
+ *                are grouped by expert, then source rank, then token
+ *   recv_scales  fp32 [N_a][H/128] out (e4m3 only, else NULL)
+ *   handle       host out: see moe_handle
+ * Errors: MOE_ERR_INVALID_ARG (NULL pointer, scales given for bf16 or missing
+ * for e4m3, misaligned workspace), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        void* workspace, size_t workspace_bytes,
+                        void* send_buf, float* send_scales, void* recv_buf, float* recv_scales,
+                        moe_handle* handle, void* stream);
+
+/* Expert stub, standing in for the grouped GEMM that reads the
+ * expert-contiguous receive rows ([A2A] 5.2: the receive layout is the expert
+ * kernel's input; [EP] worked example: each rank runs its local experts on
+ * what it received).  For receive row q of expert e:
+ *   expert_out[q] = bf16( deq(recv[q]) * m_e ),  m_e = (E + e) / E in fp32,
+ * deq = the bf16 value, or the fp32 product code * scale for e4m3 rows; each
+ * product rounds to fp32 and the result rounds once to bf16 (nearest even).
+ *   expert_out   bf16 [N_a][H] out, in receive order
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_STALE_HANDLE, MOE_ERR_HIP. */
+moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf,
+                           const float* recv_scales, uint16_t* expert_out, void* stream);
+
+/* Combine ([EP] "Combine 不是简单把结果发回来": outputs go back to their source
+ * token by the handle, never in arrival order, and are summed with the router
+ * weights; [PPLX] combine sends unquantised 16-bit activations back and the
+ * receiver writes the weighted sum into a caller-allocated tensor).
+ *   expert_out   bf16 [N_a][H] from the expert stage, in receive order
+ *   topk_w       fp32 [T][k], the source side's routing weights
+ *   comb_buf     bf16 [N_a][H] out: the reverse exchange; row t*k + j holds
+ *                the output of assignment (t, j)
+ *   y            bf16 [T][H] out: y[t] = bf16(acc), acc = fma(w[t][j],
+ *                comb[t*k+j], acc) over j = 0..k-1 from acc = 0 in fp32
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_STALE_HANDLE, MOE_ERR_HIP. */
+moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
+                       const float* topk_w, uint16_t* comb_buf, uint16_t* y, void* stream);
+
+/* ---- diagnostics ---------------------------------------------------------- */
+
+/* Static, human-readable text of a status code. */
+const char* moe_status_string(moe_status status);
+/* Text of the last HIP error this thread saw inside the library ("" if none). */
+const char* moe_last_error(void);
+
+/* Per-kernel timing: between moe_timing_begin and moe_timing_end every kernel
+ * the ctx launches is bracketed by two HIP events on its stream.
+ * moe_timing_end waits for the recorded events, writes up to `max` records
+ * (one per kernel name, in first-launch order) and returns how many kernels
+ * were seen in *count.  Timing adds two event records per launch. */
+moe_status moe_timing_begin(moe_ctx* ctx);
+moe_status moe_timing_end(moe_ctx* ctx, moe_kernel_time* out, int32_t max, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

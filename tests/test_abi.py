@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+its host-side validation returns the documented codes.  No call here reaches a
+kernel launch (every case fails or finishes before one)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+@pytest.fixture(scope="module")
+def b():
+    from combine_router_softmax_expert_amd import binding
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(b):
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(b.lib, n), n
+
+
+def _create(b, P=4, Tp=16, E=8, k=2, H=256, dt=0):
+    s = b.MoeShape(P, Tp, E, k, H, dt)
+    h = ctypes.c_void_p()
+    st = b.lib.moe_ctx_create(ctypes.byref(s), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(P=0), -1), (dict(Tp=-1), -1), (dict(E=6, P=4), -1), (dict(k=0), -1), (dict(k=9, E=8), -1),
+    (dict(H=4), -1), (dict(H=260), -1), (dict(dt=2), -1),
+    (dict(E=2048, P=4), -2), (dict(k=33, E=64), -2), (dict(dt=1, H=200), -2), (dict(H=131072), -2),
+    (dict(P=1, Tp=1 << 28, k=8), -2),
+])
+def test_ctx_create_rejects_bad_shapes(b, args, code):
+    st, h = _create(b, **args)
+    assert st == code and not h.value
+
+
+def test_ctx_sizes(b):
+    st, h = _create(b, P=8, Tp=16, E=256, k=8, H=7168, dt=0)
+    assert st == 0
+    try:
+        assert b.lib.moe_dispatch_row_bytes(h) == 2 * 7168
+        assert b.lib.moe_scales_per_row(h) == 0
+        assert b.lib.moe_num_assignments(h) == 128 * 8
+        ws = b.lib.moe_workspace_bytes(h)
+        # counts/offsets + 4 int32 arrays of N_a + 2 handle records of 16 B per assignment
+        assert ws >= 4 * (3 * 8 * 256 + 256 + 257 + 9 + 64) + 4 * 4 * 1024 + 2 * 16 * 1024
+        assert ws % 256 == 0
+    finally:
+        b.lib.moe_ctx_destroy(h)
+    st, h = _create(b, P=8, Tp=256, E=64, k=2, H=7168, dt=1)
+    assert st == 0
+    assert b.lib.moe_dispatch_row_bytes(h) == 7168 and b.lib.moe_scales_per_row(h) == 56
+    b.lib.moe_ctx_destroy(h)
+
+
+def test_status_strings(b):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert b.lib.moe_status_string(code)
+    assert b.lib.moe_status_string(7) == b"unknown status"
+
+
+def test_null_arguments(b):
+    assert b.lib.moe_ctx_create(None, None) == -1
+    st, h = _create(b)
+    fake = ctypes.c_void_p(1 << 20)  # an aligned non-null address that is never dereferenced
+    handle = b.MoeHandle()
+    assert b.lib.moe_route_topk(None, fake, fake, fake, None) == -1
+    assert b.lib.moe_route_topk(h, None, fake, fake, None) == -1
+    ws = b.lib.moe_workspace_bytes(h)
+    D = b.lib.moe_dispatch
+    assert D(None, fake, fake, fake, fake, ws, fake, None, fake, None, ctypes.byref(handle), None) == -1
+    assert D(h, fake, fake, fake, fake, ws, fake, None, fake, None, None, None) == -1
+    assert D(h, None, fake, fake, fake, ws, fake, None, fake, None, ctypes.byref(handle), None) == -1
+    assert D(h, fake, fake, fake, None, ws, fake, None, fake, None, ctypes.byref(handle), None) == -1
+    # misaligned workspace
+    assert D(h, fake, fake, fake, ctypes.c_void_p((1 << 20) + 4), ws, fake, None, fake, None,
+             ctypes.byref(handle), None) == -1
+    # workspace too small
+    assert D(h, fake, fake, fake, fake, ws - 1, fake, None, fake, None, ctypes.byref(handle), None) == -3
+    # bf16 dispatch must not be given scales
+    assert D(h, fake, fake, fake, fake, ws, fake, fake, fake, fake, ctypes.byref(handle), None) == -1
+    b.lib.moe_ctx_destroy(h)
+    st, h8 = _create(b, dt=1)
+    ws8 = b.lib.moe_workspace_bytes(h8)
+    # e4m3 dispatch needs both scale arrays
+    assert b.lib.moe_dispatch(h8, fake, fake, fake, fake, ws8, fake, None, fake, fake,
+                              ctypes.byref(handle), None) == -1
+    b.lib.moe_ctx_destroy(h8)
+
+
+def test_stale_and_foreign_handles(b):
+    st, h = _create(b)
+    st2, h2 = _create(b)
+    fake = ctypes.c_void_p(1 << 20)
+    blank = b.MoeHandle()
+    assert b.lib.moe_expert_stub(h, ctypes.byref(blank), fake, None, fake, None) == -4
+    assert b.lib.moe_combine(h, ctypes.byref(blank), fake, fake, fake, fake, None) == -4
+    assert b.lib.moe_expert_stub(h, None, fake, None, fake, None) == -1
+    # a handle of another context is foreign
+    other = b.MoeHandle()
+    other.ctx = h2.value
+    other.generation = 1
+    assert b.lib.moe_combine(h, ctypes.byref(other), fake, fake, fake, fake, None) == -4
+    b.lib.moe_ctx_destroy(h)
+    b.lib.moe_ctx_destroy(h2)
+
+
+def test_zero_tokens_is_a_noop_and_generations_advance(b):
+    st, h = _create(b, Tp=0)
+    assert st == 0
+    fake = ctypes.c_void_p(1 << 20)
+    ws = b.lib.moe_workspace_bytes(h)
+    assert b.lib.moe_route_topk(h, None, None, None, None) == 0
+    h1, h2 = b.MoeHandle(), b.MoeHandle()
+    assert b.lib.moe_dispatch(h, None, None, None, fake, ws, None, None, None, None, ctypes.byref(h1), None) == 0
+    assert h1.generation == 1 and h1.ctx == h.value
+    assert b.lib.moe_expert_stub(h, ctypes.byref(h1), None, None, None, None) == 0
+    assert b.lib.moe_combine(h, ctypes.byref(h1), None, None, None, None, None) == 0
+    assert b.lib.moe_dispatch(h, None, None, None, fake, ws, None, None, None, None, ctypes.byref(h2), None) == 0
+    assert h2.generation == 2
+    # the first handle is stale once a newer dispatch reused the workspace
+    assert b.lib.moe_combine(h, ctypes.byref(h1), None, None, None, None, None) == -4
+    assert b.lib.moe_combine(h, ctypes.byref(h2), None, None, None, None, None) == 0
+    b.lib.moe_ctx_destroy(h)
+
+
+def test_timing_without_launches(b):
+    st, h = _create(b)
+    assert b.lib.moe_timing_begin(h) == 0
+    recs = (b.MoeKernelTime * 4)()
+    n = ctypes.c_int32(-1)
+    assert b.lib.moe_timing_end(h, recs, 4, ctypes.byref(n)) == 0 and n.value == 0
+    b.lib.moe_ctx_destroy(h)

@@ -1,0 +1,214 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Integer and byte outputs (ids, counts, offsets, count
+matrix, positions, handle records, send/receive rows, FP8 codes and scales,
+expert outputs, combine rows) must match bit for bit; routing weights within
+2^-19 relative; combined outputs within |d| <= 2^-8 |ref| + 1e-6 of the
+oracle's fp32 sum, and bit for bit when both sides use the same weights."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+from combine_router_softmax_expert_amd import workloads as wl
+from gpu_helpers import (assert_integer_parts_equal, assert_weights_close, assert_y_close, bf16_to_f32, log,
+                         run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label=""):
+    log(f"[parity] {label} P={sh.P} T={sh.T} E={sh.E} k={sh.k} H={sh.H} fp8={sh.fp8} "
+        f"{'route' if ids is None else 'given ids'}")
+    if ids is None:
+        o_ids, o_w = orc.route(sh, logits)
+    else:
+        o_ids, o_w = ids, w
+    g = run_gpu(sh, x, logits=logits, ids=ids, w=w)
+    assert np.array_equal(g["ids"], o_ids)
+    if ids is None:
+        assert_weights_close(g["w"], o_w)
+    else:
+        assert np.array_equal(g["w"], o_w)
+    o = orc.run(sh, x, ids=o_ids, w=o_w)
+    assert_integer_parts_equal(g, o)
+    for key in ("send_rows", "recv_rows", "send_scales", "recv_scales", "expert_out", "comb"):
+        if o[key] is None:
+            continue
+        assert np.array_equal(g[key].view(np.uint8), o[key].view(np.uint8)), key
+    assert np.array_equal(g["send_meta"]["weight"], g["w"].ravel()[np.argsort(g["send_pos"].ravel())])
+    assert_y_close(g["y"], o["y32"])
+    if np.array_equal(g["w"], o_w):
+        assert np.array_equal(g["y"], o["y"])
+    return g, o
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_workload_parity(orc, name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=name)
+
+
+def test_workload_parity_with_oracle_routing(orc):
+    # the oracle's ids and weights fed to the GPU dispatch: everything bit-exact
+    w = wl.WORKLOADS["c3"]
+    sh = orc.Shape.of(w)
+    inp = wl.make_inputs(w)
+    ids, wt = orc.route(sh, inp["logits"])
+    g, o = _full_parity(orc, sh, inp["x"], ids=ids, w=wt, label="c3 oracle routing")
+    assert np.array_equal(g["y"], o["y"])
+
+
+def test_skewed_workload_full_size_sampled(orc):
+    # c5 at its full size, in the launch configuration the benchmark times: all
+    # routing, counts, offsets, positions and handle records in full; payload,
+    # stub and combine on sampled tokens that the oracle computes one by one
+    w = wl.WORKLOADS["c5"]
+    sh = orc.Shape.of(w)
+    log("[parity] c5 full size, generating inputs")
+    inp = wl.make_inputs(w)
+    o_ids, o_w = orc.route(sh, inp["logits"])
+    g = run_gpu(sh, inp["x"], logits=inp["logits"])
+    assert np.array_equal(g["ids"], o_ids)
+    assert_weights_close(g["w"], o_w)
+    o = orc.dispatch(sh, inp["x"], o_ids, o_w, payload=False)
+    assert_integer_parts_equal(g, o)
+    n = np.sort(o["N"])[::-1]
+    assert 0.40 <= n[: w.num_experts // 10].sum() / n.sum() <= 0.50
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([[0, sh.T - 1], rng.integers(0, sh.T, 48)]))
+    nb = sh.H // 128
+    stub_rows = np.empty((len(tokens), sh.k, sh.H), np.uint16)
+    for r, t in enumerate(tokens):
+        q, sc = orc.quantize_row(sh.H, inp["x"][t])
+        for j in range(sh.k):
+            p, qq = o["send_pos"][t, j], o["recv_pos"][t, j]
+            assert np.array_equal(g["send_rows"][p], q) and np.array_equal(g["recv_rows"][qq], q)
+            assert np.array_equal(g["send_scales"][p], sc) and np.array_equal(g["recv_scales"][qq], sc)
+            e = int(o_ids[t, j])
+            stub_rows[r, j] = orc.stub_row(sh, e, q, sc)
+            assert np.array_equal(g["expert_out"][qq], stub_rows[r, j])
+            assert np.array_equal(g["comb"][t * sh.k + j], stub_rows[r, j])
+    red = orc.reduce_tokens(sh, tokens, stub_rows, o_w)
+    assert_y_close(g["y"][tokens], red["y32"])
+    if np.array_equal(g["w"][tokens], o_w[tokens]):
+        assert np.array_equal(g["y"][tokens], red["y"])
+    del nb
+
+
+def test_worked_example_on_gpu(orc):
+    from conftest import read_golden
+    recs = read_golden("ep_top2_worked_example.txt")
+    ids = np.array([[int(v) for v in r[2:]] for r in recs if r[0] == "route"], np.int32)
+    T, k = ids.shape
+    sh = orc.Shape(4, T, 8, k, 8, False)
+    x = np.repeat(wl.float32_to_bf16_bits(np.arange(1, T + 1, dtype=np.float32))[:, None], 8, axis=1)
+    g, _ = _full_parity(orc, sh, x, ids=ids, w=np.full((T, k), 0.5, np.float32), label="worked example")
+    for r in recs:
+        if r[0] == "recv":
+            e, toks = int(r[2]), [int(v) for v in r[3:]]
+            seg = g["recv_meta"][g["expert_off"][e]:g["expert_off"][e + 1]]
+            assert [int(m["src_rank"]) * 2 + int(m["src_token"]) for m in seg] == toks
+
+
+# --------------------------------------------------------------------------
+# edge cases of the page's correctness list: all local, all to one remote
+# rank, extreme skew, empty experts, token counts that are not a multiple of
+# any tile, top-1 / top-2 / top-8, plus sizes and formats
+# --------------------------------------------------------------------------
+
+EDGE = [
+    # name, P, Tp, E, k, H, fp8
+    ("all-local-P1", 1, 33, 8, 2, 256, False),
+    ("ragged-Tp1", 4, 1, 8, 2, 136, False),
+    ("ragged-Tp7-top1", 3, 7, 6, 1, 64, False),
+    ("ragged-Tp257-top8", 8, 257, 64, 8, 384, True),
+    ("tiny-H8", 2, 5, 4, 4, 8, False),
+    ("k-equals-E", 2, 9, 4, 4, 128, True),
+    ("count-chunks-Tp3000", 2, 3000, 256, 8, 64, False),
+    ("E1024-top32", 4, 40, 1024, 32, 128, True),
+    ("E-odd-96", 3, 50, 96, 5, 520, False),
+]
+
+
+@pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(orc, name, P, Tp, E, k, H, fp8):
+    sh = orc.Shape(P, P * Tp, E, k, H, fp8)
+    seed = zlib.crc32(name.encode())
+    x = wl.make_hidden(seed, sh.T, H)
+    logits = wl.make_logits(seed, sh.T, E)
+    _full_parity(orc, sh, x, logits=logits, label=name)
+
+
+def test_all_tokens_to_one_remote_rank_and_empty_experts(orc):
+    P, Tp, E, k, H = 4, 20, 16, 2, 256
+    sh = orc.Shape(P, P * Tp, E, k, H, False)
+    T = sh.T
+    ids = np.stack([np.full(T, E - 1), np.full(T, E - 2)], axis=1).astype(np.int32)  # all to rank P-1
+    w = np.tile(np.float32([0.75, 0.25]), (T, 1))
+    g, _ = _full_parity(orc, sh, wl.make_hidden(3, T, H), ids=ids, w=w, label="one remote rank")
+    assert np.count_nonzero(g["N"]) == 2 and g["C"][:, P - 1].sum() == T * k
+
+
+def test_extreme_skew_and_ties_in_logits(orc):
+    P, Tp, E, k, H = 4, 64, 32, 4, 128
+    sh = orc.Shape(P, P * Tp, E, k, H, True)
+    rng = np.random.default_rng(9)
+    logits = rng.integers(-2, 3, size=(sh.T, E)).astype(np.float32)   # many exact ties
+    logits[:, :3] += 8.0                                              # three hot experts
+    logits[::7] = 0.0                                                 # whole rows of ties
+    logits[1, 5] = -0.0
+    _full_parity(orc, sh, wl.make_hidden(4, sh.T, H), logits=logits, label="skew+ties")
+
+
+def test_fp8_special_blocks(orc):
+    # zero blocks (scale 0, signed zeros), blocks whose amax is 448 (scale exactly
+    # 1, so every e4m3 tie is decided by the rounding rule), tiny and huge values
+    P, Tp, E, k, H = 2, 8, 4, 2, 512
+    sh = orc.Shape(P, P * Tp, E, k, H, True)
+    T = sh.T
+    x = wl.make_hidden(5, T, H)
+    x[0, :128] = 0
+    x[0, 5] = 0x8000
+    codes = np.arange(0x00, 0x7F, dtype=np.uint8)
+    import torch
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    row = np.concatenate([mids, -mids[:1], [448.0]]).astype(np.float32)[:128]
+    x[1, 128:256] = wl.float32_to_bf16_bits(row)
+    x[1, 255] = wl.float32_to_bf16_bits(np.float32([448.0]))[0]
+    x[2, 256:384] = wl.float32_to_bf16_bits(np.full(128, 1e-30, np.float32))
+    x[3, 384:512] = wl.float32_to_bf16_bits(np.linspace(-3e38, 3e38, 128).astype(np.float32))
+    logits = wl.make_logits(6, T, E)
+    _full_parity(orc, sh, x, logits=logits, label="fp8 special blocks")
+
+
+def test_deterministic_and_sentinel_free(orc):
+    w = wl.WORKLOADS["c1"]
+    sh = orc.Shape.of(w)
+    inp = wl.make_inputs(w)
+    a = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=True)
+    b = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=False, repeat=2)
+    for key in ("ids", "w", "send_rows", "recv_rows", "expert_out", "comb", "y", "send_pos", "recv_pos"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_combine_identity_top1_expert0(orc):
+    P, Tp, E, H = 4, 33, 8, 136
+    sh = orc.Shape(P, P * Tp, E, 1, H, False)
+    x = wl.make_hidden(8, sh.T, H)
+    g = run_gpu(sh, x, ids=np.zeros((sh.T, 1), np.int32), w=np.ones((sh.T, 1), np.float32))
+    assert np.array_equal(g["y"], x)
+
+
+def test_zero_tokens(orc):
+    from combine_router_softmax_expert_amd import binding as B
+    import torch
+    ctx = B.Context(4, 0, 8, 2, 256, False)
+    bufs = ctx.allocate()
+    h = B.moe_dispatch(ctx, torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), bufs["topk_ids"],
+                       bufs["topk_w"], bufs["workspace"], bufs["send"], None, bufs["recv"], None)
+    B.moe_expert_stub(ctx, h, bufs["recv"], None, bufs["expert_out"])
+    B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
+    torch.cuda.synchronize()
