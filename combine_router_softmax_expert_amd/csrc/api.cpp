@@ -224,7 +224,8 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
     moe_status s = MOE_OK;
     if (d.T > 0) {
         s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
-        if (s == MOE_OK) s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        if (s == MOE_OK && !moe::count_is_single(d))
+            s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
         if (s == MOE_OK)
             s = launch(ctx, "pack", st, [&] {
                 return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, st);

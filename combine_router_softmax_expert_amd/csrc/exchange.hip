@@ -10,16 +10,15 @@
 // receive row q goes to combine row (s*T/P + i)*k + j of the (s, i, j) its
 // record names.
 //
-// Rows are moved whole with 16-byte loads and stores, U units per thread with
-// all loads issued before the stores; a workgroup slice covers a row or part
+// Rows are moved whole with 16-byte loads and stores, one unit per thread (a
+// second load in flight before the stores runs 4x slower on gfx950 when the
+// buffers sit in the last-level cache); a workgroup slice covers a row or part
 // of one, so the permutation costs one index (or record) load per row.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
-
-constexpr int kU = 2;
 
 struct Rec { int32_t src_rank, src_token; int16_t slot, local_expert; float weight; };
 
@@ -32,18 +31,8 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
     const int p = blockIdx.x / slices;
     const int slice = blockIdx.x - p * slices;
     const int q = send_to_recv[p];
-    const int base = slice * blockDim.x * kU + threadIdx.x;
-    uint4 v[kU];
-#pragma unroll
-    for (int r = 0; r < kU; ++r) {
-        const int u = base + r * blockDim.x;
-        if (u < L) v[r] = send[(size_t)p * L + u];
-    }
-#pragma unroll
-    for (int r = 0; r < kU; ++r) {
-        const int u = base + r * blockDim.x;
-        if (u < L) recv[(size_t)q * L + u] = v[r];
-    }
+    const int u = slice * blockDim.x + threadIdx.x;
+    if (u < L) recv[(size_t)q * L + u] = send[(size_t)p * L + u];
     if (slice == 0) {
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
         if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
@@ -58,18 +47,8 @@ __global__ __launch_bounds__(512) void reverse_exchange_kernel(const uint4* __re
     const int slice = blockIdx.x - q * slices;
     const Rec m = recv_meta[q];
     const long long c = ((long long)m.src_rank * Tp + m.src_token) * k + m.slot;
-    const int base = slice * blockDim.x * kU + threadIdx.x;
-    uint4 v[kU];
-#pragma unroll
-    for (int r = 0; r < kU; ++r) {
-        const int u = base + r * blockDim.x;
-        if (u < L) v[r] = expert_out[(size_t)q * L + u];
-    }
-#pragma unroll
-    for (int r = 0; r < kU; ++r) {
-        const int u = base + r * blockDim.x;
-        if (u < L) comb[(size_t)c * L + u] = v[r];
-    }
+    const int u = slice * blockDim.x + threadIdx.x;
+    if (u < L) comb[(size_t)c * L + u] = expert_out[(size_t)q * L + u];
 }
 
 }  // namespace
@@ -78,8 +57,8 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
                            void* recv, float* recv_scales, hipStream_t st) {
     if (d.Na == 0) return hipSuccess;
     const int L = d.row_units;
-    const int B = pick_block((L + kU - 1) / kU);
-    const int slices = (L + B * kU - 1) / (B * kU);
+    const int B = pick_block(L);
+    const int slices = (L + B - 1) / B;
     hipLaunchKernelGGL(exchange_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), ws.send_to_recv,
                        send_scales, recv_scales, reinterpret_cast<const uint4*>(ws.send_meta),
@@ -91,8 +70,8 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
                                    hipStream_t st) {
     if (d.Na == 0) return hipSuccess;
     const int L = d.out_units;
-    const int B = pick_block((L + kU - 1) / kU);
-    const int slices = (L + B * kU - 1) / (B * kU);
+    const int B = pick_block(L);
+    const int slices = (L + B - 1) / B;
     hipLaunchKernelGGL(reverse_exchange_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
                        reinterpret_cast<const Rec*>(ws.recv_meta), d.Tp, d.k, L, slices);

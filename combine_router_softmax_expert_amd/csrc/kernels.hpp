@@ -21,7 +21,7 @@ struct Workspace {         // device arrays carved from the caller's workspace
     int32_t* expert_off;   // [E+1]
     int32_t* rank_recv_off;// [P+1]
     int32_t* send_off;     // [P][E]
-    int32_t* recv_off;     // [E][P]
+    int32_t* recv_off;     // [P][E]
     int32_t* C;            // [P][P]
     int32_t* bucket_rank;  // [T*k] rank of the assignment inside its (source, expert) bucket
     int32_t* send_pos;     // [T*k]
@@ -53,8 +53,7 @@ inline int pick_block(long long n) {
     return 256;
 }
 
-// LDS bytes / words-per-expert choice of the count kernel (shared with the host checks)
-int count_words_per_expert(int E, int Tp);
-size_t count_lds_bytes(int E, int W);
+// True when one workgroup does count and scan together (launch_scan is then not needed).
+bool count_is_single(const Dims& d);
 
 }  // namespace moe

@@ -13,7 +13,7 @@
 // copied k times.  FP8: a lane owns 16 channels, 8 lanes a 128-channel block;
 // amax by xor shuffles, scale = amax / 448 (fp32 division), code =
 // e4m3(x / scale) (fp32 division, nearest even).  The positions of the k
-// assignments are send_off[s][e] + bucket rank and recv_off[e][s] + bucket
+// assignments are send_off[s][e] + bucket rank and recv_off[s][e] + bucket
 // rank; the first slice also writes the handle record, the position arrays and
 // the send -> receive map that the exchange uses.
 #include "device.hpp"
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
         const int p = send_off[s * E + e] + br;
         pos[tid] = p;
         if (slice == 0) {
-            const int q = recv_off[e * P + s] + br;
+            const int q = recv_off[s * E + e] + br;
             send_pos[a] = p;
             recv_pos[a] = q;
             send_to_recv[p] = q;

@@ -6,13 +6,17 @@
 // section "Dispatch 前为什么必须 count 和 permute" fixes the output as
 // [num_tokens, top_k] ids and weights.
 //
-// A group of G lanes of one wavefront owns a token (G = 64 for E > 32, else the
-// next power of two >= E, so small-E routers put 64/G tokens in a wave).  Each
-// lane holds V = ceil(E / G) logits, loaded with the group's lanes on
-// consecutive addresses.  Top-k is k rounds of a group arg-max over 64-bit keys
-// (order-preserving logit bits, then the complemented expert id, so that equal
-// logits pick the lower id) by xor-butterfly shuffles; the winner's lane drops
-// it.  Softmax is strictly increasing, so selecting by logit is selecting by
+// E > 32: one wavefront per token, lane l holding logits l, l+64, ... (V = E/64
+// rounded up), loaded on consecutive addresses.  Each of the k rounds takes the
+// wave maximum with DPP row operations (pairs, quads, half rows, rows, then
+// row broadcasts; a few cycles each, no LDS traffic), then a ballot per slot v
+// finds the lowest expert id holding that value, so equal logits pick the lower
+// id; the winner is replaced by NaN, which the IEEE maximum ignores.
+// E <= 32: a group of G lanes (the next power of two >= E) owns a token, 64/G
+// tokens per wave, and each round is a group arg-max over 64-bit keys
+// (order-preserving logit bits, then the complemented expert id) by
+// xor-butterfly shuffles.
+// Softmax is strictly increasing, so selecting by logit is selecting by
 // probability, and the renormalised weight p_j / sum_sel p equals
 // exp(l_j - l_max) / sum_sel exp(l_i - l_max): the full partition function
 // cancels.  Those k exponentials and the slot-order sum run in double, so the
@@ -79,6 +83,75 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     }
 }
 
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), Ctrl, RowMask, 0xF, false));
+}
+
+// Maximum over the 64 lanes (IEEE maxNum: NaN lanes are ignored), in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));          // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));          // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));         // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));         // row_mirror
+    v = fmaxf(v, dpp<0x142, 0xA>(v));    // row_bcast15 into rows 1 and 3
+    v = fmaxf(v, dpp<0x143, 0xC>(v));    // row_bcast31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __restrict__ logits,
+                                                              int32_t* __restrict__ ids, float* __restrict__ w,
+                                                              int T, int E, int k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= T) return;                  // whole waves leave together
+    const float nan = __int_as_float(0x7FC00000);
+    float val[V];
+    const float* row = logits + (size_t)t * E;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int e = lane + kWave * v;
+        val[v] = e < E ? row[e] : nan;
+    }
+    double m = 0.0, sum = 0.0, my_e = 0.0;
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
+        float lm = val[0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) lm = fmaxf(lm, val[v]);
+        const float M = wave_max(lm);
+        int id = 0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const unsigned long long hit = __ballot(val[v] == M);
+            if (hit) { id = kWave * v + __ffsll((long long)hit) - 1; break; }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (lane + kWave * v == id) val[v] = nan;
+        const double lv = (double)M;
+        if (j == 0) m = lv;
+        const double ej = exp(lv - m);
+        sum += ej;                       // slot order
+        if (lane == j) { my_id = id; my_e = ej; }
+    }
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_id;
+        w[(size_t)t * k + lane] = (float)(my_e / sum);
+    }
+}
+
+template <int V>
+hipError_t launch_rtw(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st) {
+    constexpr int kThreads = 256;
+    const int tokens_per_block = kThreads / kWave;
+    const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
+    hipLaunchKernelGGL((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
+                       d.k);
+    return hipGetLastError();
+}
+
 template <int G, int V>
 hipError_t launch_rt(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st) {
     constexpr int kThreads = 256;
@@ -100,11 +173,11 @@ hipError_t launch_route_topk(const Dims& d, const float* logits, int32_t* ids, f
     if (E <= 8) return launch_rt<8, 1>(d, logits, ids, w, st);
     if (E <= 16) return launch_rt<16, 1>(d, logits, ids, w, st);
     if (E <= 32) return launch_rt<32, 1>(d, logits, ids, w, st);
-    if (E <= 64) return launch_rt<64, 1>(d, logits, ids, w, st);
-    if (E <= 128) return launch_rt<64, 2>(d, logits, ids, w, st);
-    if (E <= 256) return launch_rt<64, 4>(d, logits, ids, w, st);
-    if (E <= 512) return launch_rt<64, 8>(d, logits, ids, w, st);
-    return launch_rt<64, 16>(d, logits, ids, w, st);
+    if (E <= 64) return launch_rtw<1>(d, logits, ids, w, st);
+    if (E <= 128) return launch_rtw<2>(d, logits, ids, w, st);
+    if (E <= 256) return launch_rtw<4>(d, logits, ids, w, st);
+    if (E <= 512) return launch_rtw<8>(d, logits, ids, w, st);
+    return launch_rtw<16>(d, logits, ids, w, st);
 }
 
 }  // namespace moe

@@ -98,7 +98,7 @@ typedef struct {
     const int32_t* count_matrix;        /* [P][P]  C[s][r], rows sent from s to r */
     const int32_t* rank_expert_counts;  /* [P][E]  n[s][e] */
     const int32_t* send_offsets;        /* [P][E]  first send row of bucket (s -> e) */
-    const int32_t* recv_offsets;        /* [E][P]  first receive row of bucket (s -> e) */
+    const int32_t* recv_offsets;        /* [P][E]  first receive row of bucket (s -> e) */
     const int32_t* send_pos;            /* [T][k]  send row of assignment (t, j) */
     const int32_t* recv_pos;            /* [T][k]  receive row of assignment (t, j) */
     const moe_meta* send_meta;          /* [N_a]   record of each send row */

@@ -151,15 +151,19 @@ def test_all_tokens_to_one_remote_rank_and_empty_experts(orc):
     assert np.count_nonzero(g["N"]) == 2 and g["C"][:, P - 1].sum() == T * k
 
 
-def test_extreme_skew_and_ties_in_logits(orc):
-    P, Tp, E, k, H = 4, 64, 32, 4, 128
+@pytest.mark.parametrize("E,k", [(32, 4), (96, 8), (256, 8)])
+def test_extreme_skew_and_ties_in_logits(orc, E, k):
+    # both router shapes (lane groups for E <= 32, whole waves above)
+    P, Tp, H = 4, 64, 128
     sh = orc.Shape(P, P * Tp, E, k, H, True)
     rng = np.random.default_rng(9)
     logits = rng.integers(-2, 3, size=(sh.T, E)).astype(np.float32)   # many exact ties
     logits[:, :3] += 8.0                                              # three hot experts
     logits[::7] = 0.0                                                 # whole rows of ties
-    logits[1, 5] = -0.0
-    _full_parity(orc, sh, wl.make_hidden(4, sh.T, H), logits=logits, label="skew+ties")
+    logits[1, 5] = -0.0                                               # -0 ties with +0
+    logits[2, 1:] = -np.inf                                           # masked experts
+    logits[3, ::2] = -np.inf
+    _full_parity(orc, sh, wl.make_hidden(4, sh.T, H), logits=logits, label=f"skew+ties E={E}")
 
 
 def test_fp8_special_blocks(orc):
