@@ -88,6 +88,73 @@ def load_traffic(config: str, kernel: str):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
+KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the path
+    ("route_topk", "route_topk"), ("count_scan_single_kernel", "count"), ("count_kernel", "count"),
+    ("scan_kernel", "scan"), ("pack_kernel", "pack"), ("reverse_exchange_kernel", "reverse_exchange"),
+    ("exchange_kernel", "exchange"), ("stub_kernel", "stub"), ("reduce_kernel", "reduce"),
+)
+
+
+def path_kernel(rocprof_name: str):
+    for frag, k in KERNEL_NAME_PATTERNS:
+        if frag in rocprof_name:
+            return k
+    return None
+
+
+def _counter_means(d: str, counter: str) -> dict:
+    """Mean value per dispatch of one counter for every kernel in a rocprofv3 --pmc csv output dir."""
+    import csv
+    import glob
+    sums, cnts = {}, {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r["Kernel_Name"]
+                sums[name] = sums.get(name, 0.0) + float(r["Counter_Value"])
+                cnts[name] = cnts.get(name, 0) + 1
+    return {n: sums[n] / cnts[n] for n in sums}
+
+
+def ingest_counters(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                    copy_bytes: int, command: str):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the path's kernels, each scaled by
+    known bytes / counter reading of a plain copy, into profiles/traffic.json."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    cf = max(_counter_means(copy_fetch_dir, "FETCH_SIZE").values())
+    cw = max(_counter_means(copy_write_dir, "WRITE_SIZE").values())
+    f_fac, w_fac = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    rec = {}
+    for name, kib in fetch.items():
+        k = path_kernel(name)
+        if k is None or name not in write:
+            continue
+        rec[k] = {"fetch_bytes": round(kib * 1024 * f_fac), "write_bytes": round(write[name] * 1024 * w_fac),
+                  "fetch_kib_per_dispatch": round(kib, 1), "write_kib_per_dispatch": round(write[name], 1),
+                  "copy_factor_fetch": round(f_fac, 4), "copy_factor_write": round(w_fac, 4),
+                  "source_sha": source_sha(k), "command": command}
+    data[config] = rec
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps({"config": config, "copy_factor_fetch": f_fac, "copy_factor_write": w_fac,
+                      "kernels": {k: v["fetch_bytes"] + v["write_bytes"] for k, v in rec.items()}}))
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size (read nbytes, write nbytes) for counter calibration."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
 def cpu_baseline(w, inp, budget_s: float) -> dict:
     """The oracle, as it stands, on one host core over a bounded sample of the workload."""
     import numpy as np
@@ -138,12 +205,25 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc outputs into profiles/traffic.json for --config")
+    ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        ingest_counters(args.config, *args.ingest_counters, copy_bytes=1 << 30, command=args.counter_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the expert-parallel ranks are emulated in one HBM "
               "and nothing here uses a second GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch

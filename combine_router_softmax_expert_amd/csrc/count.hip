@@ -233,10 +233,14 @@ __global__ __launch_bounds__(kThreads) void count_scan_single_kernel(
         }
     }
     __syncthreads();
-    segmented_word_prefix(bitmap, prefix, PE * W, W);
-    __syncthreads();
+    if (W > 1) {
+        segmented_word_prefix(bitmap, prefix, PE * W, W);
+        __syncthreads();
+    } else {
+        for (int x = tid; x < PE; x += bs) prefix[x] = 0;
+    }
     for (int x = tid; x < PE; x += bs) {
-        const int c = word_total(bitmap, prefix, x, W);
+        const int c = W > 1 ? word_total(bitmap, prefix, x, W) : __popc(bitmap[x]);
         nl[x] = c;
         n_out[x] = c;
     }
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void count_scan_single_kernel(
                 const int c = e < E ? nl[s * E + e] : 0;
                 const int incl = wave_inclusive_scan(c);
                 if (e < E) send_off[(size_t)s * E + e] = carry + incl - c;
-                carry += __shfl(incl, kWave - 1, kWave);
+                carry += __builtin_amdgcn_readlane(incl, kWave - 1);
             }
         }
     }

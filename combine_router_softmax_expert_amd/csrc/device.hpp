@@ -71,14 +71,27 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // ---- wave helpers ---------------------------------------------------------------
 
+// DPP move of v (row_mask / bank_mask select the lanes written; the others, and
+// lanes whose source falls outside the row, read 0).
+template <int Ctrl, int RowMask = 0xF, int BankMask = 0xF>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, Ctrl, RowMask, BankMask, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: sums of the last 1..4
+// lanes within each 16-lane row (row_shr 1, 2, 3), then row_shr 4 and 8 into
+// the upper banks complete each row, and row_bcast15 / row_bcast31 carry rows
+// into the next ones.  Seven DPP adds, no LDS traffic.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
+    int x = v;
+    x += dpp_or_zero<0x111>(v);              // row_shr:1
+    x += dpp_or_zero<0x112>(v);              // row_shr:2
+    x += dpp_or_zero<0x113>(v);              // row_shr:3
+    x += dpp_or_zero<0x114, 0xF, 0xE>(x);    // row_shr:4 into lanes 4..15 of each row
+    x += dpp_or_zero<0x118, 0xF, 0xC>(x);    // row_shr:8 into lanes 8..15
+    x += dpp_or_zero<0x142, 0xA>(x);         // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);         // row_bcast:31 into rows 2 and 3
+    return x;
 }
 
 // Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
