@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -32,7 +33,7 @@ struct moe_ctx {
     moe::Dims d;
     // byte offsets of the workspace arrays
     size_t o_n, o_N, o_expert_off, o_rank_recv_off, o_send_off, o_recv_off, o_C, o_bucket_rank, o_send_pos,
-        o_recv_pos, o_send_to_recv, o_send_meta, o_recv_meta, ws_bytes;
+        o_recv_pos, o_send_to_recv, o_recv_to_send, o_send_meta, o_recv_meta, ws_bytes;
     uint64_t generation = 0;
     bool timing = false;
     std::vector<TimingRecord> records;
@@ -92,6 +93,7 @@ moe::Workspace carve(const moe_ctx* ctx, void* base) {
     w.send_pos = reinterpret_cast<int32_t*>(p + ctx->o_send_pos);
     w.recv_pos = reinterpret_cast<int32_t*>(p + ctx->o_recv_pos);
     w.send_to_recv = reinterpret_cast<int32_t*>(p + ctx->o_send_to_recv);
+    w.recv_to_send = reinterpret_cast<int32_t*>(p + ctx->o_recv_to_send);
     w.send_meta = p + ctx->o_send_meta;
     w.recv_meta = p + ctx->o_recv_meta;
     return w;
@@ -101,6 +103,7 @@ moe::Workspace carve(const moe_ctx* ctx, void* base) {
 moe::Workspace from_handle(const moe_handle* h) {
     moe::Workspace w{};
     w.rank_recv_off = const_cast<int32_t*>(h->rank_recv_offsets);
+    w.recv_pos = const_cast<int32_t*>(h->recv_pos);
     w.recv_meta = const_cast<moe_meta*>(h->recv_meta);
     return w;
 }
@@ -162,6 +165,12 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
     d.row_units = fp8 ? s.hidden / 16 : s.hidden / 8;
     d.out_units = s.hidden / 8;
     d.scales = fp8 ? s.hidden / kFp8Block : 0;
+    // MOE_EP_CACHE_POLICY=temporal|streaming overrides the size-based choice (for A/B measurements)
+    d.policy = moe::CachePolicy::kAuto;
+    if (const char* pol = std::getenv("MOE_EP_CACHE_POLICY")) {
+        if (std::strcmp(pol, "temporal") == 0) d.policy = moe::CachePolicy::kTemporal;
+        if (std::strcmp(pol, "streaming") == 0) d.policy = moe::CachePolicy::kStreaming;
+    }
 
     const size_t P = d.P, E = d.E, tk = (size_t)Na;
     size_t off = 0;
@@ -177,6 +186,7 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
     ctx->o_send_pos = take(4 * tk);
     ctx->o_recv_pos = take(4 * tk);
     ctx->o_send_to_recv = take(4 * tk);
+    ctx->o_recv_to_send = take(4 * tk);
     ctx->o_send_meta = take(sizeof(moe_meta) * tk);
     ctx->o_recv_meta = take(sizeof(moe_meta) * tk);
     ctx->ws_bytes = off;

@@ -4,16 +4,19 @@
 // Forward ("[Infra-10] All-to-All Optimization" 1: all-to-all as a distributed
 // transpose, rank j receives piece j of every rank; "Expert Parallel: MoE
 // Token ..." worked example: each rank's receive region is grouped by local
-// expert): send row p lands on receive row send_to_recv[p] together with its
-// FP8 scales and its handle record.  Reverse ("Combine 不是简单把结果发回来":
+// expert): send row p lands on receive row q = send_to_recv[p] together with
+// its FP8 scales and its handle record.  Reverse ("Combine 不是简单把结果发回来":
 // outputs go back to their token by the handle, never in arrival order):
 // receive row q goes to combine row (s*T/P + i)*k + j of the (s, i, j) its
-// record names.
+// record names, which is the row whose recv_pos is q.
 //
-// Rows are moved whole with 16-byte loads and stores, one unit per thread (a
-// second load in flight before the stores runs 4x slower on gfx950 when the
-// buffers sit in the last-level cache); a workgroup slice covers a row or part
-// of one, so the permutation costs one index (or record) load per row.
+// Rows move whole with 16-byte loads and stores, one unit per thread (a second
+// load in flight before the stores runs 4x slower on gfx950 when the buffers
+// sit in the last-level cache); a workgroup slice covers a row or part of one,
+// so the permutation costs one index (or record) load per row.  Two forms:
+//  - temporal (buffers that stay in cache): walk the source rows and scatter;
+//  - streaming (large buffers): walk the destination rows in order, gather
+//    from the source, nontemporal loads and stores (~18% faster there).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -22,33 +25,47 @@ namespace {
 
 struct Rec { int32_t src_rank, src_token; int16_t slot, local_expert; float weight; };
 
+template <bool GATHER>
 __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
-                                                       const int32_t* __restrict__ send_to_recv,
+                                                       const int32_t* __restrict__ map,
                                                        const float* __restrict__ send_scales,
                                                        float* __restrict__ recv_scales,
                                                        const uint4* __restrict__ send_meta,
                                                        uint4* __restrict__ recv_meta, int L, int nb, int slices) {
-    const int p = blockIdx.x / slices;
-    const int slice = blockIdx.x - p * slices;
-    const int q = send_to_recv[p];
+    const int b = blockIdx.x / slices;
+    const int slice = blockIdx.x - b * slices;
+    const int o = map[b];                       // GATHER: send row of receive row b; else receive row of send row b
+    const int p = GATHER ? o : b;
+    const int q = GATHER ? b : o;
     const int u = slice * blockDim.x + threadIdx.x;
-    if (u < L) recv[(size_t)q * L + u] = send[(size_t)p * L + u];
+    if (u < L) st16<GATHER>(&recv[(size_t)q * L + u], ld16<GATHER>(&send[(size_t)p * L + u]));
     if (slice == 0) {
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
         if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
     }
 }
 
-__global__ __launch_bounds__(512) void reverse_exchange_kernel(const uint4* __restrict__ expert_out,
-                                                               uint4* __restrict__ comb,
-                                                               const Rec* __restrict__ recv_meta, int Tp, int k,
-                                                               int L, int slices) {
+__global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uint4* __restrict__ expert_out,
+                                                                       uint4* __restrict__ comb,
+                                                                       const Rec* __restrict__ recv_meta, int Tp,
+                                                                       int k, int L, int slices) {
     const int q = blockIdx.x / slices;
     const int slice = blockIdx.x - q * slices;
     const Rec m = recv_meta[q];
     const long long c = ((long long)m.src_rank * Tp + m.src_token) * k + m.slot;
     const int u = slice * blockDim.x + threadIdx.x;
     if (u < L) comb[(size_t)c * L + u] = expert_out[(size_t)q * L + u];
+}
+
+__global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint4* __restrict__ expert_out,
+                                                                      uint4* __restrict__ comb,
+                                                                      const int32_t* __restrict__ recv_pos, int L,
+                                                                      int slices) {
+    const int c = blockIdx.x / slices;          // combine row t*k + j
+    const int slice = blockIdx.x - c * slices;
+    const int q = recv_pos[c];
+    const int u = slice * blockDim.x + threadIdx.x;
+    if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
 }
 
 }  // namespace
@@ -59,10 +76,13 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int L = d.row_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    hipLaunchKernelGGL(exchange_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), ws.send_to_recv,
-                       send_scales, recv_scales, reinterpret_cast<const uint4*>(ws.send_meta),
-                       reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales, slices);
+    const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
+    auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+                       reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
+                       gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
+                       reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L,
+                       d.scales, slices);
     return hipGetLastError();
 }
 
@@ -72,9 +92,14 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int L = d.out_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    hipLaunchKernelGGL(reverse_exchange_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                       reinterpret_cast<const Rec*>(ws.recv_meta), d.Tp, d.k, L, slices);
+    if (streaming(d, 2LL * d.Na * 16LL * L))
+        hipLaunchKernelGGL(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
+                           slices);
+    else
+        hipLaunchKernelGGL(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
+                           reinterpret_cast<const Rec*>(ws.recv_meta), d.Tp, d.k, L, slices);
     return hipGetLastError();
 }
 

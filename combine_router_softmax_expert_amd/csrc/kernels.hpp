@@ -6,8 +6,14 @@
 
 namespace moe {
 
+// Cache policy of the payload kernels: kAuto streams (nontemporal accesses, gather
+// form of the exchanges) when a kernel moves at least kStreamingBytes.
+enum class CachePolicy { kAuto = 0, kTemporal = 1, kStreaming = 2 };
+constexpr long long kStreamingBytes = 128LL << 20;
+
 struct Dims {
     int P, Tp, T, E, Ep, k, H;
+    CachePolicy policy;
     bool fp8;
     long long Na;          // T * k
     int row_units;         // 16-byte units per dispatched row (2H/16 or H/16)
@@ -26,7 +32,8 @@ struct Workspace {         // device arrays carved from the caller's workspace
     int32_t* bucket_rank;  // [T*k] rank of the assignment inside its (source, expert) bucket
     int32_t* send_pos;     // [T*k]
     int32_t* recv_pos;     // [T*k]
-    int32_t* send_to_recv; // [N_a]
+    int32_t* send_to_recv; // [N_a] receive row of each send row
+    int32_t* recv_to_send; // [N_a] send row of each receive row
     void* send_meta;       // [N_a] 16-byte records
     void* recv_meta;       // [N_a]
 };
@@ -43,6 +50,10 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out,
                                    uint16_t* comb, hipStream_t st);
 hipError_t launch_reduce(const Dims& d, const uint16_t* comb, const float* w, uint16_t* y, hipStream_t st);
+
+inline bool streaming(const Dims& d, long long bytes) {
+    return d.policy == CachePolicy::kStreaming || (d.policy == CachePolicy::kAuto && bytes >= kStreamingBytes);
+}
 
 // Threads per block for a row of `n` per-thread work items: the whole row when it
 // fits in 512 threads, else a divisor of n from 512 down to 256, else 256.

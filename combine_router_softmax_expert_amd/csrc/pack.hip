@@ -12,10 +12,12 @@
 // and written to its k send rows; the FP8 form is computed once per token and
 // copied k times.  FP8: a lane owns 16 channels, 8 lanes a 128-channel block;
 // amax by xor shuffles, scale = amax / 448 (fp32 division), code =
-// e4m3(x / scale) (fp32 division, nearest even).  The positions of the k
+// e4m3(x / scale) (fp32 division, then v_cvt_pk_fp8_f32: nearest even).  The positions of the k
 // assignments are send_off[s][e] + bucket rank and recv_off[s][e] + bucket
 // rank; the first slice also writes the handle record, the position arrays and
-// the send -> receive map that the exchange uses.
+// the send <-> receive maps that the exchange uses.  Large problems load x
+// nontemporally; the k row stores stay temporal (nontemporal stores of k = 8
+// scattered rows ran at 60% of the temporal bandwidth on gfx950).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -31,7 +33,7 @@ struct Meta {
 };
 static_assert(sizeof(Meta) == 16, "handle record is 16 bytes");
 
-template <bool FP8>
+template <bool FP8, bool NTL = false, bool NTS = false>
 __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
                                                    const float* __restrict__ w,
                                                    const int32_t* __restrict__ bucket_rank,
@@ -39,6 +41,7 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
                                                    const int32_t* __restrict__ recv_off,
                                                    uint4* __restrict__ send, float* __restrict__ send_scales,
                                                    Meta* __restrict__ send_meta, int32_t* __restrict__ send_to_recv,
+                                                   int32_t* __restrict__ recv_to_send,
                                                    int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
                                                    int Tp, int E, int Ep, int P, int k, int L, int slices) {
     __shared__ int32_t pos[32];
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
             send_pos[a] = p;
             recv_pos[a] = q;
             send_to_recv[p] = q;
+            recv_to_send[q] = p;
             Meta m;
             m.src_rank = s;
             m.src_token = t - s * Tp;
@@ -74,8 +78,8 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
         // lanes u..u+7 share a 128-channel block; L % 8 == 0 and blocks start at
         // multiples of 64 lanes, so a block's lanes are all valid or all not
         if (u >= L) return;
-        const uint4 a = x[(size_t)t * (2 * L) + 2 * u];
-        const uint4 b = x[(size_t)t * (2 * L) + 2 * u + 1];
+        const uint4 a = ld16<NTL>(&x[(size_t)t * (2 * L) + 2 * u]);
+        const uint4 b = ld16<NTL>(&x[(size_t)t * (2 * L) + 2 * u + 1]);
         float f[16];
         {
             float lo[8], hi[8];
@@ -91,25 +95,31 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
         amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
         amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
         const float scale = amax / 448.0f;
-        uint32_t q[4] = {0u, 0u, 0u, 0u};
+        uint32_t q[4];
+        if (amax == 0.0f) {                       // all zeros: scale 0, codes keep each zero's sign
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t c;
-            if (amax == 0.0f) c = (__float_as_uint(f[i]) >> 24) & 0x80u;   // signed zero
-            else c = e4m3_from_f32(f[i] / scale);
-            q[i >> 2] |= c << (8 * (i & 3));
+            for (int w4 = 0; w4 < 4; ++w4) {
+                q[w4] = 0u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[w4] |= ((__float_as_uint(f[4 * w4 + i]) >> 24) & 0x80u) << (8 * i);
+            }
+        } else {
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4)
+                q[w4] = pack4_e4m3(f[4 * w4] / scale, f[4 * w4 + 1] / scale, f[4 * w4 + 2] / scale,
+                                   f[4 * w4 + 3] / scale);
         }
         const uint4 out = make_uint4(q[0], q[1], q[2], q[3]);
         const int nb = L / 8;
         for (int j = 0; j < k; ++j) {
             const int p = pos[j];
-            send[(size_t)p * L + u] = out;
+            st16<NTS>(&send[(size_t)p * L + u], out);
             if ((u & 7) == 0) send_scales[(size_t)p * nb + (u >> 3)] = scale;
         }
     } else {
         if (u >= L) return;
-        const uint4 v = x[(size_t)t * L + u];
-        for (int j = 0; j < k; ++j) send[(size_t)pos[j] * L + u] = v;
+        const uint4 v = ld16<NTL>(&x[(size_t)t * L + u]);
+        for (int j = 0; j < k; ++j) st16<NTS>(&send[(size_t)pos[j] * L + u], v);
     }
 }
 
@@ -122,16 +132,13 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     const long long blocks = (long long)d.T * slices;
-    if (d.fp8)
-        hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(B), 0, st,
-                           reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
-                           reinterpret_cast<uint4*>(send), send_scales, reinterpret_cast<Meta*>(ws.send_meta),
-                           ws.send_to_recv, ws.send_pos, ws.recv_pos, d.Tp, d.E, d.Ep, d.P, d.k, L, slices);
-    else
-        hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(B), 0, st,
-                           reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
-                           reinterpret_cast<uint4*>(send), send_scales, reinterpret_cast<Meta*>(ws.send_meta),
-                           ws.send_to_recv, ws.send_pos, ws.recv_pos, d.Tp, d.E, d.Ep, d.P, d.k, L, slices);
+    const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));
+    auto kernel = d.fp8 ? (nt ? pack_kernel<true, true, false> : pack_kernel<true, false, false>)
+                        : (nt ? pack_kernel<false, true, false> : pack_kernel<false, false, false>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(B), 0, st, reinterpret_cast<const uint4*>(x), ids, w,
+                       ws.bucket_rank, ws.send_off, ws.recv_off, reinterpret_cast<uint4*>(send), send_scales,
+                       reinterpret_cast<Meta*>(ws.send_meta), ws.send_to_recv, ws.recv_to_send, ws.send_pos,
+                       ws.recv_pos, d.Tp, d.E, d.Ep, d.P, d.k, L, slices);
     return hipGetLastError();
 }
 

@@ -7,7 +7,8 @@
 // the global expert of receive row q: local expert from the row's handle record
 // and owner rank from the receive-region offsets (a wave ballot over
 // rank_recv_off).  deq is the bf16 value itself, or code * scale in fp32 for
-// e4m3 rows (lane = 16 codes of one 128-channel block).  Each product rounds
+// e4m3 rows (lane = 16 codes of one 128-channel block, decoded exactly by
+// v_cvt_pk_f32_fp8).  Each product rounds
 // to fp32 and the result once to bf16.
 #include "device.hpp"
 #include "kernels.hpp"
@@ -29,7 +30,11 @@ __device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_
     return count - 1;
 }
 
-template <bool FP8>
+// bf16 rows: one lane per 16-byte unit in and out.  e4m3 rows: one lane per 16
+// codes (a 16-byte load) and two 16-byte stores; with half-width (8-byte) code
+// loads instead, the kernel ran ~25% slower on gfx950, and the split stores must
+// stay temporal (nontemporal ones cannot merge the half-lines and ran ~40% slower).
+template <bool FP8, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
                                                    const Rec* __restrict__ meta,
                                                    const int32_t* __restrict__ rank_recv_off,
@@ -43,26 +48,28 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
     const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
     if (u >= L) return;
     if (FP8) {
-        const uint4 c = recv[(size_t)q * L + u];
+        const uint4 c = ld16<NTL>(&recv[(size_t)q * L + u]);
         const float sc = scales[(size_t)q * (L / 8) + (u >> 3)];
-        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
         float f[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float d = e4m3_to_f32((words[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sc;
-            f[i] = d * m;
-        }
+        unpack4_e4m3(c.x, f);
+        unpack4_e4m3(c.y, f + 4);
+        unpack4_e4m3(c.z, f + 8);
+        unpack4_e4m3(c.w, f + 12);
         float lo[8], hi[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { lo[i] = f[i]; hi[i] = f[8 + i]; }
-        out[(size_t)q * (2 * L) + 2 * u] = pack8_bf16(lo);
-        out[(size_t)q * (2 * L) + 2 * u + 1] = pack8_bf16(hi);
+        for (int i = 0; i < 8; ++i) {
+            const float a = f[i] * sc, b = f[8 + i] * sc;
+            lo[i] = a * m;
+            hi[i] = b * m;
+        }
+        st16<NTS>(&out[(size_t)q * (2 * L) + 2 * u], pack8_bf16(lo));
+        st16<NTS>(&out[(size_t)q * (2 * L) + 2 * u + 1], pack8_bf16(hi));
     } else {
         float f[8];
-        unpack8_bf16(recv[(size_t)q * L + u], f);
+        unpack8_bf16(ld16<NTL>(&recv[(size_t)q * L + u]), f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = f[i] * m;
-        out[(size_t)q * L + u] = pack8_bf16(f);
+        st16<NTS>(&out[(size_t)q * L + u], pack8_bf16(f));
     }
 }
 
@@ -75,14 +82,13 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     const dim3 grid((unsigned)(d.Na * slices));
-    if (d.fp8)
-        hipLaunchKernelGGL(stub_kernel<true>, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
-                           reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off,
-                           reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, slices);
-    else
-        hipLaunchKernelGGL(stub_kernel<false>, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
-                           reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off,
-                           reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, slices);
+    const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
+    // streaming: e4m3 rows load nontemporally, bf16 rows store nontemporally (best of the four choices each)
+    auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, false> : stub_kernel<true, false, false>)
+                        : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
+    hipLaunchKernelGGL(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+                       reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
+                       d.P, d.E, d.Ep, L, slices);
     return hipGetLastError();
 }
 

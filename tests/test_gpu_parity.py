@@ -50,6 +50,16 @@ def test_workload_parity(orc, name):
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=name)
 
 
+@pytest.mark.parametrize("policy,name", [("streaming", "c1"), ("streaming", "c3"), ("temporal", "c4")])
+def test_workload_parity_other_cache_policy(orc, monkeypatch, policy, name):
+    # the size-based choice picks one form per kernel; force the other one
+    # (streaming: gather-form exchanges and nontemporal accesses) on the same data
+    monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {policy}")
+
+
 def test_workload_parity_with_oracle_routing(orc):
     # the oracle's ids and weights fed to the GPU dispatch: everything bit-exact
     w = wl.WORKLOADS["c3"]
@@ -132,8 +142,10 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("policy", ["auto", "streaming"])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_shapes(orc, name, P, Tp, E, k, H, fp8):
+def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy):
+    monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
     sh = orc.Shape(P, P * Tp, E, k, H, fp8)
     seed = zlib.crc32(name.encode())
     x = wl.make_hidden(seed, sh.T, H)
