@@ -49,6 +49,14 @@ def build() -> str:
 _lib = None
 
 
+def use_library(path: str):
+    """Load the oracle from another build of moe_oracle.c (the mutation tests use it)."""
+    global _lib, _LIB_PATH
+    _LIB_PATH = path
+    _lib = None
+    return lib()
+
+
 def lib():
     global _lib
     if _lib is None:

@@ -115,7 +115,7 @@ def test_byte_model_closed_form(orc):
 # invariants of the page's correctness section, on every workload shape
 # --------------------------------------------------------------------------
 
-def _check_invariants(sh, ids, d):
+def _check_invariants(sh, ids, d, w=None):
     P, T, E, k = sh.P, sh.T, sh.E, sh.k
     Tp, Ep, Na = T // P, E // P, T * k
     # assignment conservation
@@ -131,6 +131,8 @@ def _check_invariants(sh, ids, d):
     assert np.array_equal(m["src_rank"].astype(np.int64) * Tp + m["src_token"], t)
     assert np.array_equal(m["slot"], j)
     assert np.array_equal(m["local_expert"], ids.ravel() % Ep)
+    if w is not None:                      # the record carries its own assignment's weight
+        assert np.array_equal(m["weight"], np.asarray(w, np.float32).ravel())
     # ownership: every row of rank r's receive region belongs to an expert of r
     for r in range(P):
         lo, hi = d["rank_recv_off"][r], d["rank_recv_off"][r + 1]
@@ -157,7 +159,7 @@ def test_invariants_on_workloads(orc, name):
     ids, wt = orc.route(sh, logits)
     x = np.zeros((w.tokens, w.hidden), np.uint16)
     d = orc.dispatch(sh, x, ids, wt, payload=False)
-    _check_invariants(sh, ids, d)
+    _check_invariants(sh, ids, d, wt)
 
 
 def _brute_positions(P, T, k, ids):
@@ -197,10 +199,11 @@ def test_positions_brute_force_random(orc, P, Tp, E, k):
     T = P * Tp
     ids = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
     sh = orc.Shape(P, T, E, k, 8, False)
-    d = orc.dispatch(sh, np.zeros((T, 8), np.uint16), ids, np.ones((T, k), np.float32), payload=False)
+    w = rng.random((T, k)).astype(np.float32)
+    d = orc.dispatch(sh, np.zeros((T, 8), np.uint16), ids, w, payload=False)
     bs, br = _brute_positions(P, T, k, ids)
     assert np.array_equal(d["send_pos"], bs) and np.array_equal(d["recv_pos"], br)
-    _check_invariants(sh, ids, d)
+    _check_invariants(sh, ids, d, w)
 
 
 # --------------------------------------------------------------------------
@@ -295,6 +298,21 @@ def test_combine_closed_form(orc, name):
     assert np.all(np.abs(out["y32"] - ref) <= k * 2.0 ** -24 * mag + 1e-300)
     # y is y32 rounded once to bf16
     assert np.array_equal(out["y"], orc.bf16_from_double(out["y32"].astype(np.float64)))
+
+
+def test_reduce_slot_order_closed_form(orc):
+    # fp32 accumulation in slot order from 0: acc = fma(w0, v0, 0) rounds
+    # RN(1/3) * 3 = 1 + 2^-25 to 1.0, then fma(1.0, -1.0, 1.0) = 0 exactly.  The
+    # other order keeps the 2^-25 (fma(w0, v0, -1) is exact), so this pins the order.
+    H = 8
+    w0 = np.float32(1.0) / np.float32(3.0)
+    assert float(w0) * 3.0 == 1.0 + 2.0 ** -25
+    comb = np.stack([wl.float32_to_bf16_bits(np.full(H, 3.0, np.float32)),
+                     wl.float32_to_bf16_bits(np.full(H, -1.0, np.float32))])[None]
+    w = np.array([[w0, 1.0]], np.float32)
+    r = orc.reduce_tokens(orc.Shape(1, 1, 2, 2, H, False), [0], comb, w)
+    assert np.all(r["y32"] == 0.0) and np.all(r["y"] == 0)
+    assert np.all(r["y64"] == 2.0 ** -25)       # the exact sum, for contrast
 
 
 def test_stub_closed_form_bf16(orc):
