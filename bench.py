@@ -32,10 +32,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s vs peak, H=7168 E=256 
 KERNEL_SOURCES = {
     "route_topk": "route.hip", "count": "count.hip", "scan": "count.hip", "pack": "pack.hip",
     "exchange": "exchange.hip", "stub": "stub.hip", "reverse_exchange": "exchange.hip", "reduce": "reduce.hip",
+    "pack_direct": "pack.hip", "reduce_direct": "reduce.hip",
 }
 PHASE_OF = {
     "route_topk": "route", "count": "dispatch", "scan": "dispatch", "pack": "dispatch", "exchange": "dispatch",
     "stub": "expert_stub", "reverse_exchange": "combine", "reduce": "combine",
+    "pack_direct": "dispatch", "reduce_direct": "combine",
 }
 
 
@@ -55,6 +57,8 @@ def kernel_bytes(w) -> dict:
         "stub": Na * D + Na * 2 * H,
         "reverse_exchange": 2 * Na * 2 * H,
         "reduce": Na * 2 * H + 2 * H * T,
+        "pack_direct": 2 * H * T + Na * D,          # rows land straight in the receive buffer
+        "reduce_direct": Na * 2 * H + 2 * H * T,    # reads the expert output through the handle
     }
 
 
@@ -202,6 +206,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--mode", default="base", choices=["base", "direct"],
+                    help="base: pack into send buffers + exchange copies; direct: pack straight into the "
+                         "receive rows and reduce straight from the expert output")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
@@ -241,8 +248,10 @@ def main():
     logits = torch.from_numpy(inp["logits"]).to(dev)
     stream = torch.cuda.current_stream()
 
+    direct = args.mode == "direct"
+
     def step():
-        B.run_path(ctx, bufs, x, logits, stream)
+        B.run_path(ctx, bufs, x, logits, stream, direct=direct)
 
     for _ in range(args.warmup):
         step()
@@ -319,7 +328,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "ranks": w.num_ranks, "tokens": T, "experts": w.num_experts,
                    "top_k": w.top_k, "hidden": w.hidden, "dispatch": w.dispatch_dtype,
-                   "parallelism": f"ep{w.num_ranks} emulated on 1 GPU"},
+                   "parallelism": f"ep{w.num_ranks} emulated on 1 GPU", "mode": args.mode},
         "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "dispatch_combine": {
             "ms": round(dc_ms, 5), "tokens_per_s": round(T / (dc_ms * 1e-3), 1),

@@ -66,6 +66,8 @@ def _load():
         "moe_dispatch": (I32, [P, P, P, P, P, SZ, P, P, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_expert_stub": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_combine": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
+        "moe_dispatch_direct": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
+        "moe_combine_direct": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_begin": (I32, [P]),
@@ -231,6 +233,33 @@ def moe_combine(ctx: Context, handle: MoeHandle, expert_out, topk_w, comb_buf, y
            "moe_combine")
 
 
+def moe_dispatch_direct(ctx: Context, x, topk_ids, topk_w, workspace, recv_buf, recv_scales,
+                        stream=None) -> MoeHandle:
+    import torch
+    T, H, k, Na = ctx.T, ctx.H, ctx.k, ctx.num_assignments
+    rb, nb = ctx.row_bytes, ctx.scales_per_row
+    h = MoeHandle()
+    ws = _ptr(workspace, None, ctx.workspace_bytes, "workspace")
+    _check(lib.moe_dispatch_direct(ctx.handle_ptr, _ptr(x, (torch.bfloat16, torch.int16), 2 * T * H, "x"),
+                                   _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                                   _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                   ws, workspace.numel() * workspace.element_size(),
+                                   _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                                   _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"),
+                                   ctypes.byref(h), _stream(stream)), "moe_dispatch_direct")
+    return h
+
+
+def moe_combine_direct(ctx: Context, handle: MoeHandle, expert_out, topk_w, y, stream=None):
+    import torch
+    Na, H, T, k = ctx.num_assignments, ctx.H, ctx.T, ctx.k
+    _check(lib.moe_combine_direct(ctx.handle_ptr, ctypes.byref(handle),
+                                  _ptr(expert_out, (torch.bfloat16, torch.int16), 2 * Na * H, "expert_out"),
+                                  _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                  _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
+           "moe_combine_direct")
+
+
 def moe_timing_begin(ctx: Context):
     _check(lib.moe_timing_begin(ctx.handle_ptr), "moe_timing_begin")
 
@@ -242,11 +271,18 @@ def moe_timing_end(ctx: Context) -> dict:
     return {recs[i].kernel.decode(): (recs[i].launches, recs[i].total_ms) for i in range(min(n.value, 64))}
 
 
-def run_path(ctx: Context, bufs: dict, x, logits, stream=None) -> MoeHandle:
-    """One pass of the whole path: route, dispatch, expert stub, combine."""
+def run_path(ctx: Context, bufs: dict, x, logits, stream=None, direct: bool = False) -> MoeHandle:
+    """One pass of the whole path: route, dispatch, expert stub, combine (direct forms if asked)."""
     moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"], stream)
-    h = moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
-                     bufs["send_scales"], bufs["recv"], bufs["recv_scales"], stream)
+    if direct:
+        h = moe_dispatch_direct(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
+                                bufs["recv_scales"], stream)
+    else:
+        h = moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                         bufs["send_scales"], bufs["recv"], bufs["recv_scales"], stream)
     moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"], stream)
-    moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+    if direct:
+        moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"], stream)
+    else:
+        moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
     return h

@@ -108,6 +108,26 @@ moe::Workspace from_handle(const moe_handle* h) {
     return w;
 }
 
+// Publishes a dispatch: bumps the ctx generation and points the handle at the
+// workspace arrays (no send-side record when the rows went straight to their
+// receive rows).
+void fill_handle(moe_ctx* ctx, const moe::Workspace& ws, moe_handle* handle, bool with_send) {
+    ctx->generation += 1;
+    handle->expert_counts = ws.N;
+    handle->expert_offsets = ws.expert_off;
+    handle->rank_recv_offsets = ws.rank_recv_off;
+    handle->count_matrix = ws.C;
+    handle->rank_expert_counts = ws.n;
+    handle->send_offsets = ws.send_off;
+    handle->recv_offsets = ws.recv_off;
+    handle->send_pos = ws.send_pos;
+    handle->recv_pos = ws.recv_pos;
+    handle->send_meta = with_send ? static_cast<const moe_meta*>(ws.send_meta) : nullptr;
+    handle->recv_meta = static_cast<const moe_meta*>(ws.recv_meta);
+    handle->ctx = ctx;
+    handle->generation = ctx->generation;
+}
+
 moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
     if (!h) return MOE_ERR_INVALID_ARG;
     if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0) return MOE_ERR_STALE_HANDLE;
@@ -238,7 +258,7 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
             s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
         if (s == MOE_OK)
             s = launch(ctx, "pack", st, [&] {
-                return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, st);
+                return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, false, st);
             });
         if (s == MOE_OK)
             s = launch(ctx, "exchange", st, [&] {
@@ -246,20 +266,33 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
             });
         if (s != MOE_OK) return s;
     }
-    ctx->generation += 1;
-    handle->expert_counts = ws.N;
-    handle->expert_offsets = ws.expert_off;
-    handle->rank_recv_offsets = ws.rank_recv_off;
-    handle->count_matrix = ws.C;
-    handle->rank_expert_counts = ws.n;
-    handle->send_offsets = ws.send_off;
-    handle->recv_offsets = ws.recv_off;
-    handle->send_pos = ws.send_pos;
-    handle->recv_pos = ws.recv_pos;
-    handle->send_meta = static_cast<const moe_meta*>(ws.send_meta);
-    handle->recv_meta = static_cast<const moe_meta*>(ws.recv_meta);
-    handle->ctx = ctx;
-    handle->generation = ctx->generation;
+    fill_handle(ctx, ws, handle, true);
+    return MOE_OK;
+}
+
+moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                               void* workspace, size_t workspace_bytes, void* recv_buf, float* recv_scales,
+                               moe_handle* handle, void* stream) {
+    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const moe::Dims d = ctx->d;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return MOE_ERR_INVALID_ARG;
+
+    const moe::Workspace ws = carve(ctx, workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d.T > 0) {
+        moe_status s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
+        if (s == MOE_OK && !moe::count_is_single(d))
+            s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        if (s == MOE_OK)
+            s = launch(ctx, "pack_direct", st, [&] {
+                return moe::launch_pack(d, x, topk_ids, topk_w, ws, recv_buf, recv_scales, true, st);
+            });
+        if (s != MOE_OK) return s;
+    }
+    fill_handle(ctx, ws, handle, false);
     return MOE_OK;
 }
 
@@ -288,7 +321,22 @@ moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* e
     hipStream_t st = static_cast<hipStream_t>(stream);
     s = launch(ctx, "reverse_exchange", st, [&] { return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, st); });
     if (s != MOE_OK) return s;
-    return launch(ctx, "reduce", st, [&] { return moe::launch_reduce(d, comb_buf, topk_w, y, st); });
+    return launch(ctx, "reduce", st,
+                  [&] { return moe::launch_reduce(d, comb_buf, nullptr, topk_w, y, false, st); });
+}
+
+moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
+                              const float* topk_w, uint16_t* y, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_handle(ctx, handle);
+    if (s != MOE_OK) return s;
+    const moe::Dims d = ctx->d;
+    if (d.T == 0) return MOE_OK;
+    if (!expert_out || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch(ctx, "reduce_direct", st, [&] {
+        return moe::launch_reduce(d, expert_out, handle->recv_pos, topk_w, y, true, st);
+    });
 }
 
 moe_status moe_timing_begin(moe_ctx* ctx) {

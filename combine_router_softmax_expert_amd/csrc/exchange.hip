@@ -23,8 +23,6 @@
 namespace moe {
 namespace {
 
-struct Rec { int32_t src_rank, src_token; int16_t slot, local_expert; float weight; };
-
 template <bool GATHER>
 __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
                                                        const int32_t* __restrict__ map,
@@ -32,13 +30,22 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
                                                        float* __restrict__ recv_scales,
                                                        const uint4* __restrict__ send_meta,
                                                        uint4* __restrict__ recv_meta, int L, int nb, int slices) {
-    const int b = blockIdx.x / slices;
-    const int slice = blockIdx.x - b * slices;
-    const int o = map[b];                       // GATHER: send row of receive row b; else receive row of send row b
-    const int p = GATHER ? o : b;
-    const int q = GATHER ? b : o;
+    const int b = blockIdx.x;
+    const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;
-    if (u < L) st16<GATHER>(&recv[(size_t)q * L + u], ld16<GATHER>(&send[(size_t)p * L + u]));
+    int p, q;
+    uint4 v;
+    if (GATHER) {                               // the source row comes from the map
+        q = b;
+        p = map[b];
+        if (u < L) v = ld16<true>(&send[(size_t)p * L + u]);
+    } else {                                    // the row's data is loaded before its destination
+        p = b;                                  // index, so the two memory round trips overlap
+        if (u < L) v = send[(size_t)p * L + u];
+        __builtin_amdgcn_sched_barrier(0);
+        q = map[b];
+    }
+    if (u < L) st16<GATHER>(&recv[(size_t)q * L + u], v);
     if (slice == 0) {
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
         if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
@@ -47,22 +54,25 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
 
 __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uint4* __restrict__ expert_out,
                                                                        uint4* __restrict__ comb,
-                                                                       const Rec* __restrict__ recv_meta, int Tp,
+                                                                       const HandleRecord* __restrict__ recv_meta, int Tp,
                                                                        int k, int L, int slices) {
-    const int q = blockIdx.x / slices;
-    const int slice = blockIdx.x - q * slices;
-    const Rec m = recv_meta[q];
-    const long long c = ((long long)m.src_rank * Tp + m.src_token) * k + m.slot;
+    const int q = blockIdx.x;
+    const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;
-    if (u < L) comb[(size_t)c * L + u] = expert_out[(size_t)q * L + u];
+    uint4 v;
+    if (u < L) v = expert_out[(size_t)q * L + u];   // data first: its load overlaps the record's
+    __builtin_amdgcn_sched_barrier(0);
+    const HandleRecord m = recv_meta[q];
+    const long long c = ((long long)m.src_rank * Tp + m.src_token) * k + m.slot;
+    if (u < L) comb[(size_t)c * L + u] = v;
 }
 
 __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint4* __restrict__ expert_out,
                                                                       uint4* __restrict__ comb,
                                                                       const int32_t* __restrict__ recv_pos, int L,
                                                                       int slices) {
-    const int c = blockIdx.x / slices;          // combine row t*k + j
-    const int slice = blockIdx.x - c * slices;
+    const int c = blockIdx.x;                   // combine row t*k + j
+    const int slice = blockIdx.y;
     const int q = recv_pos[c];
     const int u = slice * blockDim.x + threadIdx.x;
     if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
@@ -78,7 +88,7 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int slices = (L + B - 1) / B;
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
                        gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
                        reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L,
@@ -93,13 +103,13 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (streaming(d, 2LL * d.Na * 16LL * L))
-        hipLaunchKernelGGL(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+        hipLaunchKernelGGL(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                            reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
                            slices);
     else
-        hipLaunchKernelGGL(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na * slices)), dim3(B), 0, st,
+        hipLaunchKernelGGL(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                            reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                           reinterpret_cast<const Rec*>(ws.recv_meta), d.Tp, d.k, L, slices);
+                           reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
     return hipGetLastError();
 }
 

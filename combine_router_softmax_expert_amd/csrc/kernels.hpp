@@ -6,6 +6,16 @@
 
 namespace moe {
 
+// The 16-byte handle record that travels with every dispatched row (the ABI's moe_meta).
+struct HandleRecord {
+    int32_t src_rank;
+    int32_t src_token;
+    int16_t slot;
+    int16_t local_expert;
+    float weight;
+};
+static_assert(sizeof(HandleRecord) == 16, "handle record is 16 bytes");
+
 // Cache policy of the payload kernels: kAuto streams (nontemporal accesses, gather
 // form of the exchanges) when a kernel moves at least kStreamingBytes.
 enum class CachePolicy { kAuto = 0, kTemporal = 1, kStreaming = 2 };
@@ -41,15 +51,18 @@ struct Workspace {         // device arrays carved from the caller's workspace
 hipError_t launch_route_topk(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st);
+// direct: rows, scales and records go straight to their receive rows (dst = the receive buffer)
 hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w,
-                       const Workspace& ws, void* send, float* send_scales, hipStream_t st);
+                       const Workspace& ws, void* dst, float* dst_scales, bool direct, hipStream_t st);
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
                            void* recv, float* recv_scales, hipStream_t st);
 hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales,
                        uint16_t* out, hipStream_t st);
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out,
                                    uint16_t* comb, hipStream_t st);
-hipError_t launch_reduce(const Dims& d, const uint16_t* comb, const float* w, uint16_t* y, hipStream_t st);
+// direct: rows = the expert output, read through recv_pos; else rows = the combine buffer
+hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
+                         bool direct, hipStream_t st);
 
 inline bool streaming(const Dims& d, long long bytes) {
     return d.policy == CachePolicy::kStreaming || (d.policy == CachePolicy::kAuto && bytes >= kStreamingBytes);

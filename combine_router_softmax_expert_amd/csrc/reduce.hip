@@ -6,7 +6,9 @@
 //
 // y[t] = bf16(acc), acc = fma(w[t][j], comb[t*k + j], acc) for j = 0..k-1 from
 // acc = 0, in fp32: the combine rows of a token are adjacent, so a lane reads
-// its 16 bytes of each of the k rows and writes 16 bytes of y.  Large problems
+// its 16 bytes of each of the k rows and writes 16 bytes of y.  The direct form
+// reads row recv_pos[t*k + j] of the expert output instead, gathering through
+// the handle with no combine buffer in between.  Large problems
 // stream (nontemporal loads, ~16% faster for k = 8 rows of 14 KiB).
 #include "device.hpp"
 #include "kernels.hpp"
@@ -14,37 +16,56 @@
 namespace moe {
 namespace {
 
-template <bool NTL, bool NTS>
-__global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ comb, const float* __restrict__ w,
-                                                     uint4* __restrict__ y, int k, int L, int slices) {
-    const int t = blockIdx.x / slices;
-    const int slice = blockIdx.x - t * slices;
-    const int u = slice * blockDim.x + threadIdx.x;
+// Up to kChunk rows are loaded before their fused multiply-adds, which still
+// run in slot order.
+constexpr int kChunk = 8;
+
+template <bool NTL, bool NTS, bool DIRECT>
+__global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
+                                                     const float* __restrict__ w, uint4* __restrict__ y, int k, int L) {
+    const int t = blockIdx.x;
+    const int u = blockIdx.y * blockDim.x + threadIdx.x;
     if (u >= L) return;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    const uint4* rows = comb + (size_t)t * k * L + u;
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        float f[8];
-        unpack8_bf16(ld16<NTL>(&rows[(size_t)j * L]), f);
+    for (int j0 = 0; j0 < k; j0 += kChunk) {
+        uint4 v[kChunk];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+        for (int j = 0; j < kChunk; ++j) {
+            if (j0 + j < k) {
+                const int a = t * k + j0 + j;               // combine row of slot j0 + j
+                const int row = DIRECT ? recv_pos[a] : a;   // direct: the expert output itself
+                v[j] = ld16<NTL>(&rows[(size_t)row * L + u]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            if (j0 + j < k) {
+                const float wj = w[(size_t)t * k + j0 + j];
+                float f[8];
+                unpack8_bf16(v[j], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+            }
+        }
     }
     st16<NTS>(&y[(size_t)t * L + u], pack8_bf16(acc));
 }
 
 }  // namespace
 
-hipError_t launch_reduce(const Dims& d, const uint16_t* comb, const float* w, uint16_t* y, hipStream_t st) {
+hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
+                         bool direct, hipStream_t st) {
     if (d.T == 0) return hipSuccess;
     const int L = d.out_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    auto kernel = streaming(d, (d.Na + d.T) * 16LL * L) ? reduce_kernel<true, true> : reduce_kernel<false, false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)((long long)d.T * slices)), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(comb), w, reinterpret_cast<uint4*>(y), d.k, L, slices);
+    const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
+    auto kernel = direct ? (nt ? reduce_kernel<true, true, true> : reduce_kernel<false, false, true>)
+                         : (nt ? reduce_kernel<true, true, false> : reduce_kernel<false, false, false>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
+                       reinterpret_cast<const uint4*>(rows), recv_pos, w, reinterpret_cast<uint4*>(y), d.k, L);
     return hipGetLastError();
 }
 

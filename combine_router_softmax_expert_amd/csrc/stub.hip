@@ -16,8 +16,6 @@
 namespace moe {
 namespace {
 
-struct Rec { int32_t src_rank, src_token; int16_t slot, local_expert; float weight; };
-
 // Rank whose receive region holds row q: the number of region starts <= q, less one.
 __device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_off, int P, int q) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -36,19 +34,21 @@ __device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_
 // stay temporal (nontemporal ones cannot merge the half-lines and ran ~40% slower).
 template <bool FP8, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
-                                                   const Rec* __restrict__ meta,
+                                                   const HandleRecord* __restrict__ meta,
                                                    const int32_t* __restrict__ rank_recv_off,
                                                    uint4* __restrict__ out, int P, int E, int Ep, int L,
                                                    int slices) {
-    const int q = blockIdx.x / slices;
-    const int slice = blockIdx.x - q * slices;
+    const int q = blockIdx.x;
+    const int slice = blockIdx.y;
+    const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
+    uint4 c = make_uint4(0u, 0u, 0u, 0u);
+    if (u < L) c = ld16<NTL>(&recv[(size_t)q * L + u]);   // issued first: overlaps the expert lookup
+    __builtin_amdgcn_sched_barrier(0);
     const int r = owner_rank(rank_recv_off, P, q);
     const int e = r * Ep + meta[q].local_expert;
     const float m = (float)(E + e) / (float)E;
-    const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
     if (u >= L) return;
     if (FP8) {
-        const uint4 c = ld16<NTL>(&recv[(size_t)q * L + u]);
         const float sc = scales[(size_t)q * (L / 8) + (u >> 3)];
         float f[16];
         unpack4_e4m3(c.x, f);
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
         st16<NTS>(&out[(size_t)q * (2 * L) + 2 * u + 1], pack8_bf16(hi));
     } else {
         float f[8];
-        unpack8_bf16(ld16<NTL>(&recv[(size_t)q * L + u]), f);
+        unpack8_bf16(c, f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = f[i] * m;
         st16<NTS>(&out[(size_t)q * L + u], pack8_bf16(f));
@@ -81,13 +81,13 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     const int L = d.row_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    const dim3 grid((unsigned)(d.Na * slices));
+    const dim3 grid((unsigned)d.Na, (unsigned)slices);
     const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
     // streaming: e4m3 rows load nontemporally, bf16 rows store nontemporally (best of the four choices each)
     auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, false> : stub_kernel<true, false, false>)
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
     hipLaunchKernelGGL(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
-                       reinterpret_cast<const Rec*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
+                       reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
                        d.P, d.E, d.Ep, L, slices);
     return hipGetLastError();
 }

@@ -197,6 +197,31 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                        const float* topk_w, uint16_t* comb_buf, uint16_t* y, void* stream);
 
+/* ---- direct forms (pack straight into the receive rows, reduce straight from
+ * the expert output) ------------------------------------------------------- */
+
+/* Dispatch that writes every row, scale and handle record straight into its
+ * receive row, with no send buffer and no separate exchange ([A2A] 4.3: the
+ * preferred form permutes the input straight into the destination buffer;
+ * [PPLX] further improvements: over a shared-memory link, buffers shared across
+ * devices remove copies).  On one GPU this models each source rank writing into
+ * its peers' receive regions.  Same counts, offsets, positions, receive rows,
+ * scales and receive records as moe_dispatch; the handle's send_meta is NULL.
+ * Arguments as moe_dispatch without send_buf / send_scales.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                               void* workspace, size_t workspace_bytes, void* recv_buf, float* recv_scales,
+                               moe_handle* handle, void* stream);
+
+/* Combine that reads each assignment's expert output through the handle
+ * (row recv_pos[t][j]) and reduces it in place of the reverse exchange, with no
+ * combine buffer ([A2A] 5.1: the combine fuses the inverse index, the weight
+ * multiply and the reduction).  y is bit-identical to moe_combine's.  Accepts a
+ * handle from either dispatch.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_STALE_HANDLE, MOE_ERR_HIP. */
+moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
+                              const float* topk_w, uint16_t* y, void* stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 
 /* Static, human-readable text of a status code. */

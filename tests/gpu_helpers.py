@@ -23,9 +23,9 @@ def _ws_view(ws, base_ptr, ptr, nbytes, dtype):
     return ws[off:off + nbytes].cpu().numpy().view(dtype)
 
 
-def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, read_payload=True):
-    """Run route (unless ids/w are given), dispatch, stub and combine on cuda:0;
-    returns numpy copies of every output."""
+def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, read_payload=True, direct=False):
+    """Run route (unless ids/w are given), dispatch, stub and combine on cuda:0
+    (the direct forms if asked); returns numpy copies of every output."""
     import torch
     from combine_router_softmax_expert_amd import binding as B
     from oracle.oracle import META_DTYPE
@@ -48,10 +48,17 @@ def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, re
     for _ in range(repeat):
         if ids is None:
             B.moe_route_topk(ctx, ld, bufs["topk_ids"], bufs["topk_w"])
-        h = B.moe_dispatch(ctx, xd, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
-                           bufs["send_scales"], bufs["recv"], bufs["recv_scales"])
+        if direct:
+            h = B.moe_dispatch_direct(ctx, xd, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
+                                      bufs["recv_scales"])
+        else:
+            h = B.moe_dispatch(ctx, xd, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                               bufs["send_scales"], bufs["recv"], bufs["recv_scales"])
         B.moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"])
-        B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
+        if direct:
+            B.moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"])
+        else:
+            B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
     torch.cuda.synchronize()
 
     ws = bufs["workspace"]
@@ -68,16 +75,16 @@ def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, re
         "recv_off": _ws_view(ws, base, h.recv_offsets, 4 * E * P, np.int32).reshape(P, E).T,
         "send_pos": _ws_view(ws, base, h.send_pos, 4 * Na, np.int32).reshape(T, k),
         "recv_pos": _ws_view(ws, base, h.recv_pos, 4 * Na, np.int32).reshape(T, k),
-        "send_meta": _ws_view(ws, base, h.send_meta, 16 * Na, META_DTYPE),
+        "send_meta": None if direct else _ws_view(ws, base, h.send_meta, 16 * Na, META_DTYPE),
         "recv_meta": _ws_view(ws, base, h.recv_meta, 16 * Na, META_DTYPE),
     }
     if read_payload:
         out.update({
-            "send_rows": bufs["send"].cpu().numpy(), "recv_rows": bufs["recv"].cpu().numpy(),
-            "send_scales": bufs["send_scales"].cpu().numpy() if shape.fp8 else None,
+            "send_rows": None if direct else bufs["send"].cpu().numpy(), "recv_rows": bufs["recv"].cpu().numpy(),
+            "send_scales": bufs["send_scales"].cpu().numpy() if shape.fp8 and not direct else None,
             "recv_scales": bufs["recv_scales"].cpu().numpy() if shape.fp8 else None,
             "expert_out": bufs["expert_out"].view(torch.int16).cpu().numpy().view(np.uint16),
-            "comb": bufs["comb"].view(torch.int16).cpu().numpy().view(np.uint16),
+            "comb": None if direct else bufs["comb"].view(torch.int16).cpu().numpy().view(np.uint16),
             "y": bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16),
         })
     else:
@@ -112,5 +119,7 @@ def assert_integer_parts_equal(g, o):
     for key in INT_KEYS:
         assert np.array_equal(g[key], o[key]), key
     for key in ("send_meta", "recv_meta"):
+        if g[key] is None:            # the direct dispatch keeps no send-side records
+            continue
         for f in ("src_rank", "src_token", "slot", "local_expert"):
             assert np.array_equal(g[key][f], o[key][f]), (key, f)

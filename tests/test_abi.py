@@ -104,6 +104,27 @@ def test_null_arguments(b):
     b.lib.moe_ctx_destroy(h8)
 
 
+def test_direct_forms_validate_arguments(b):
+    st, h = _create(b)
+    fake = ctypes.c_void_p(1 << 20)
+    ws = b.lib.moe_workspace_bytes(h)
+    handle = b.MoeHandle()
+    D = b.lib.moe_dispatch_direct
+    assert D(None, fake, fake, fake, fake, ws, fake, None, ctypes.byref(handle), None) == -1
+    assert D(h, fake, fake, fake, fake, ws, None, None, ctypes.byref(handle), None) == -1
+    assert D(h, fake, fake, fake, fake, ws - 1, fake, None, ctypes.byref(handle), None) == -3
+    assert D(h, fake, fake, fake, fake, ws, fake, fake, ctypes.byref(handle), None) == -1   # bf16 takes no scales
+    assert b.lib.moe_combine_direct(h, ctypes.byref(b.MoeHandle()), fake, fake, fake, None) == -4
+    b.lib.moe_ctx_destroy(h)
+    st, h0 = _create(b, Tp=0)
+    h1 = b.MoeHandle()
+    assert b.lib.moe_dispatch_direct(h0, None, None, None, fake, b.lib.moe_workspace_bytes(h0), None, None,
+                                     ctypes.byref(h1), None) == 0
+    assert h1.generation == 1 and not h1.send_meta
+    assert b.lib.moe_combine_direct(h0, ctypes.byref(h1), None, None, None, None) == 0
+    b.lib.moe_ctx_destroy(h0)
+
+
 def test_stale_and_foreign_handles(b):
     st, h = _create(b)
     st2, h2 = _create(b)

@@ -17,14 +17,14 @@ from gpu_helpers import (assert_integer_parts_equal, assert_weights_close, asser
 pytestmark = pytest.mark.gpu
 
 
-def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label=""):
+def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label="", direct=False):
     log(f"[parity] {label} P={sh.P} T={sh.T} E={sh.E} k={sh.k} H={sh.H} fp8={sh.fp8} "
-        f"{'route' if ids is None else 'given ids'}")
+        f"{'route' if ids is None else 'given ids'}{' direct' if direct else ''}")
     if ids is None:
         o_ids, o_w = orc.route(sh, logits)
     else:
         o_ids, o_w = ids, w
-    g = run_gpu(sh, x, logits=logits, ids=ids, w=w)
+    g = run_gpu(sh, x, logits=logits, ids=ids, w=w, direct=direct)
     assert np.array_equal(g["ids"], o_ids)
     if ids is None:
         assert_weights_close(g["w"], o_w)
@@ -33,10 +33,12 @@ def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label=""):
     o = orc.run(sh, x, ids=o_ids, w=o_w)
     assert_integer_parts_equal(g, o)
     for key in ("send_rows", "recv_rows", "send_scales", "recv_scales", "expert_out", "comb"):
-        if o[key] is None:
+        if o[key] is None or g[key] is None:
             continue
         assert np.array_equal(g[key].view(np.uint8), o[key].view(np.uint8)), key
-    assert np.array_equal(g["send_meta"]["weight"], g["w"].ravel()[np.argsort(g["send_pos"].ravel())])
+    assert np.array_equal(g["recv_meta"]["weight"], g["w"].ravel()[np.argsort(g["recv_pos"].ravel())])
+    if g["send_meta"] is not None:
+        assert np.array_equal(g["send_meta"]["weight"], g["w"].ravel()[np.argsort(g["send_pos"].ravel())])
     assert_y_close(g["y"], o["y32"])
     if np.array_equal(g["w"], o_w):
         assert np.array_equal(g["y"], o["y"])
@@ -60,6 +62,14 @@ def test_workload_parity_other_cache_policy(orc, monkeypatch, policy, name):
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {policy}")
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_workload_parity_direct(orc, name):
+    # pack straight into the receive rows, reduce straight from the expert output
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=name, direct=True)
+
+
 def test_workload_parity_with_oracle_routing(orc):
     # the oracle's ids and weights fed to the GPU dispatch: everything bit-exact
     w = wl.WORKLOADS["c3"]
@@ -70,16 +80,17 @@ def test_workload_parity_with_oracle_routing(orc):
     assert np.array_equal(g["y"], o["y"])
 
 
-def test_skewed_workload_full_size_sampled(orc):
+@pytest.mark.parametrize("direct", [False, True])
+def test_skewed_workload_full_size_sampled(orc, direct):
     # c5 at its full size, in the launch configuration the benchmark times: all
     # routing, counts, offsets, positions and handle records in full; payload,
     # stub and combine on sampled tokens that the oracle computes one by one
     w = wl.WORKLOADS["c5"]
     sh = orc.Shape.of(w)
-    log("[parity] c5 full size, generating inputs")
+    log(f"[parity] c5 full size{' direct' if direct else ''}, generating inputs")
     inp = wl.make_inputs(w)
     o_ids, o_w = orc.route(sh, inp["logits"])
-    g = run_gpu(sh, inp["x"], logits=inp["logits"])
+    g = run_gpu(sh, inp["x"], logits=inp["logits"], direct=direct)
     assert np.array_equal(g["ids"], o_ids)
     assert_weights_close(g["w"], o_w)
     o = orc.dispatch(sh, inp["x"], o_ids, o_w, payload=False)
@@ -94,12 +105,14 @@ def test_skewed_workload_full_size_sampled(orc):
         q, sc = orc.quantize_row(sh.H, inp["x"][t])
         for j in range(sh.k):
             p, qq = o["send_pos"][t, j], o["recv_pos"][t, j]
-            assert np.array_equal(g["send_rows"][p], q) and np.array_equal(g["recv_rows"][qq], q)
-            assert np.array_equal(g["send_scales"][p], sc) and np.array_equal(g["recv_scales"][qq], sc)
+            assert np.array_equal(g["recv_rows"][qq], q) and np.array_equal(g["recv_scales"][qq], sc)
+            if not direct:
+                assert np.array_equal(g["send_rows"][p], q) and np.array_equal(g["send_scales"][p], sc)
             e = int(o_ids[t, j])
             stub_rows[r, j] = orc.stub_row(sh, e, q, sc)
             assert np.array_equal(g["expert_out"][qq], stub_rows[r, j])
-            assert np.array_equal(g["comb"][t * sh.k + j], stub_rows[r, j])
+            if not direct:
+                assert np.array_equal(g["comb"][t * sh.k + j], stub_rows[r, j])
     red = orc.reduce_tokens(sh, tokens, stub_rows, o_w)
     assert_y_close(g["y"][tokens], red["y32"])
     if np.array_equal(g["w"][tokens], o_w[tokens]):
@@ -142,15 +155,15 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("policy", ["auto", "streaming"])
+@pytest.mark.parametrize("policy,direct", [("auto", False), ("streaming", False), ("auto", True)])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy):
+def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, direct):
     monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
     sh = orc.Shape(P, P * Tp, E, k, H, fp8)
     seed = zlib.crc32(name.encode())
     x = wl.make_hidden(seed, sh.T, H)
     logits = wl.make_logits(seed, sh.T, E)
-    _full_parity(orc, sh, x, logits=logits, label=name)
+    _full_parity(orc, sh, x, logits=logits, label=name, direct=direct)
 
 
 def test_all_tokens_to_one_remote_rank_and_empty_experts(orc):
