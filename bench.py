@@ -250,34 +250,56 @@ def main():
 
     direct = args.mode == "direct"
 
-    def step():
+    def step(direct=direct):
         B.run_path(ctx, bufs, x, logits, stream, direct=direct)
+
+    def dispatch_combine(direct=direct):
+        """Dispatch and combine alone (routing ids/weights and expert outputs from earlier steps)."""
+        if direct:
+            h = B.moe_dispatch_direct(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
+                                      bufs["recv_scales"], stream)
+            B.moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"], stream)
+        else:
+            h = B.moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                               bufs["send_scales"], bufs["recv"], bufs["recv_scales"], stream)
+            B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        """Mean ms of n back-to-back calls, bracketed by synchronize + events on the launch stream."""
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(n):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # timed region: K back-to-back steps of the whole path
+    ms_per_step = timed(step, args.steps)
+    # dispatch + combine alone, K times back to back
+    dc_ms = timed(dispatch_combine, args.steps)
 
     # the same K steps with every kernel bracketed by HIP events on its stream
-    # (the library records them around each launch), for per-kernel durations
+    # (the library records them around each launch), for per-kernel durations;
+    # each event pair adds launch-to-launch overhead, so these read high for
+    # kernels of a few microseconds
     B.moe_timing_begin(ctx)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_with_events = ev0.elapsed_time(ev1) / args.steps
+    ms_with_events = timed(step, args.steps)
     kt = B.moe_timing_end(ctx)
+
+    # the other form of dispatch/combine on the same data, for comparison
+    other = not direct
+    for _ in range(args.warmup):
+        step(other)
+    other_ms = timed(lambda: step(other), args.steps)
+    other_dc_ms = timed(lambda: dispatch_combine(other), args.steps)
+    step()   # leave the buffers as the measured form wrote them
 
     # per-step times with the caches flushed before each step (a 1 GiB write)
     cold_ms = None
@@ -310,9 +332,13 @@ def main():
     traffic = load_traffic(args.config, dom)
 
     T = w.tokens
-    dc_ms = phases.get("dispatch", 0.0) + phases.get("combine", 0.0)
-    dc_bytes = sum(kb[n] for n in kt if PHASE_OF[n] in ("dispatch", "combine"))
-    step_bytes = sum(kb.values())
+    dc_kernels = ("count", "scan", "pack_direct", "reduce_direct") if direct else \
+        ("count", "scan", "pack", "exchange", "reverse_exchange", "reduce")
+    dc_bytes = sum(kb[n] for n in dc_kernels if n in kt)
+    other_kernels = ("count", "scan", "pack", "exchange", "reverse_exchange", "reduce") if direct else \
+        ("count", "scan", "pack_direct", "reduce_direct")
+    other_dc_bytes = sum(kb[n] for n in other_kernels if n != "scan" or "scan" in kt)
+    step_bytes = sum(kb[n] for n in kt)
     out = {
         "metric": METRIC,
         "value": round(T / (ms_per_step * 1e-3), 1),
@@ -334,6 +360,13 @@ def main():
             "ms": round(dc_ms, 5), "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
             "algorithmic_bytes": dc_bytes, "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "other_mode": {
+            "mode": "base" if direct else "direct",
+            "ms_per_step": round(other_ms, 5), "tokens_per_s": round(T / (other_ms * 1e-3), 1),
+            "dispatch_combine_ms": round(other_dc_ms, 5),
+            "dispatch_combine_tokens_per_s": round(T / (other_dc_ms * 1e-3), 1),
+            "dispatch_combine_gbps": round(other_dc_bytes / (other_dc_ms * 1e-3) / 1e9, 1),
         },
         "phases_ms": {k: round(v, 5) for k, v in phases.items()},
         "kernels": per_kernel,
