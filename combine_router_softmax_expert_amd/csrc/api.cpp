@@ -128,6 +128,15 @@ void fill_handle(moe_ctx* ctx, const moe::Workspace& ws, moe_handle* handle, boo
     handle->generation = ctx->generation;
 }
 
+// The count kernel (and the scan kernel unless one workgroup does both).
+moe_status count_and_scan(moe_ctx* ctx, const moe::Dims& d, const int32_t* topk_ids, const moe::Workspace& ws,
+                          hipStream_t st) {
+    moe_status s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
+    if (s == MOE_OK && !moe::count_is_single(d))
+        s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+    return s;
+}
+
 moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
     if (!h) return MOE_ERR_INVALID_ARG;
     if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0) return MOE_ERR_STALE_HANDLE;
@@ -191,6 +200,10 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
         if (std::strcmp(pol, "temporal") == 0) d.policy = moe::CachePolicy::kTemporal;
         if (std::strcmp(pol, "streaming") == 0) d.policy = moe::CachePolicy::kStreaming;
     }
+    // MOE_EP_COUNT_PATH=separate keeps the count kernels for small problems too (for A/B tests)
+    d.count_path = moe::CountPath::kAuto;
+    if (const char* cp = std::getenv("MOE_EP_COUNT_PATH"))
+        if (std::strcmp(cp, "separate") == 0) d.count_path = moe::CountPath::kSeparate;
 
     const size_t P = d.P, E = d.E, tk = (size_t)Na;
     size_t off = 0;
@@ -253,11 +266,10 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
     hipStream_t st = static_cast<hipStream_t>(stream);
     moe_status s = MOE_OK;
     if (d.T > 0) {
-        s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
-        if (s == MOE_OK && !moe::count_is_single(d))
-            s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        const bool fused = moe::pack_counts(d);
+        if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
         if (s == MOE_OK)
-            s = launch(ctx, "pack", st, [&] {
+            s = launch(ctx, fused ? "count_pack" : "pack", st, [&] {
                 return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, false, st);
             });
         if (s == MOE_OK)
@@ -283,11 +295,10 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d.T > 0) {
-        moe_status s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
-        if (s == MOE_OK && !moe::count_is_single(d))
-            s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        const bool fused = moe::pack_counts(d);
+        moe_status s = fused ? MOE_OK : count_and_scan(ctx, d, topk_ids, ws, st);
         if (s == MOE_OK)
-            s = launch(ctx, "pack_direct", st, [&] {
+            s = launch(ctx, fused ? "count_pack_direct" : "pack_direct", st, [&] {
                 return moe::launch_pack(d, x, topk_ids, topk_w, ws, recv_buf, recv_scales, true, st);
             });
         if (s != MOE_OK) return s;

@@ -129,6 +129,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return x;
 }
 
+// Barrier for a block's LDS traffic only: orders its LDS accesses across the
+// barrier without draining its outstanding global loads and stores, which a
+// full __syncthreads (a workgroup release fence) waits for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
 // `tmp` needs blockDim.x / 64 + 1 ints of LDS.  Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {

@@ -21,9 +21,15 @@ static_assert(sizeof(HandleRecord) == 16, "handle record is 16 bytes");
 enum class CachePolicy { kAuto = 0, kTemporal = 1, kStreaming = 2 };
 constexpr long long kStreamingBytes = 128LL << 20;
 
+// How dispatch ranks the assignments: kAuto lets the pack kernel count by itself
+// when the problem is small enough (pack_counts), kSeparate always launches the
+// count (and scan) kernels first.
+enum class CountPath { kAuto = 0, kSeparate = 1 };
+
 struct Dims {
     int P, Tp, T, E, Ep, k, H;
     CachePolicy policy;
+    CountPath count_path;
     bool fp8;
     long long Na;          // T * k
     int row_units;         // 16-byte units per dispatched row (2H/16 or H/16)
@@ -79,5 +85,9 @@ inline int pick_block(long long n) {
 
 // True when one workgroup does count and scan together (launch_scan is then not needed).
 bool count_is_single(const Dims& d);
+
+// True when launch_pack counts and ranks the assignments itself and writes the
+// counts and offsets too (launch_count and launch_scan are then not needed).
+bool pack_counts(const Dims& d);
 
 }  // namespace moe

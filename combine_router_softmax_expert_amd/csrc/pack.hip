@@ -23,32 +23,39 @@
 // over the link and leaves no send buffer to exchange.  Large problems load x
 // nontemporally; the k row stores stay temporal (nontemporal stores of k = 8
 // scattered rows ran at 60% of the temporal bandwidth on gfx950).
+//
+// Counting form (small problems, where a separate count launch costs more than
+// the counting itself): every workgroup ranks its token's k assignments by
+// itself from all N_a expert ids, which sit in the cache.  With tokens blocked
+// by rank and each token's experts distinct, the stable positions have a
+// closed form in counts (the send order is local expert then token, the
+// receive order expert then source rank then token, as in the worked example of
+// "Expert Parallel: MoE Token ..."): for assignment (t, j) with expert e on
+// rank s,
+//   recv_pos = #{a : id_a < e} + #{a : id_a = e, token(a) < t}
+//   send_pos = s*(T/P)*k + the same two counts over rank s's assignments only.
+// Both are one compare per id against the key 2*id + [token(a) >= t] < 2e + 1:
+// the ids are staged in LDS, each lane counts a run of them for one of the k
+// slots, and xor shuffles and an LDS table sum the runs.  P extra workgroups, one per source rank,
+// write the counts and offsets of the handle (n, N, C, expert_off,
+// rank_recv_off, send_off, recv_off) from LDS histograms in the same launch.
+#include <algorithm>
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-template <bool FP8, bool NTL = false, bool NTS = false, bool DIRECT = false>
-__global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
-                                                   const float* __restrict__ w,
-                                                   const int32_t* __restrict__ bucket_rank,
-                                                   const int32_t* __restrict__ send_off,
-                                                   const int32_t* __restrict__ recv_off,
-                                                   uint4* __restrict__ dst, float* __restrict__ dst_scales,
-                                                   HandleRecord* __restrict__ dst_meta, int32_t* __restrict__ send_to_recv,
-                                                   int32_t* __restrict__ recv_to_send,
-                                                   int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
-                                                   int Tp, int E, int Ep, int P, int k, int L, int slices) {
-    __shared__ int32_t pos[32];
-    const int t = blockIdx.x;
-    const int slice = blockIdx.y;
-    const int s = t / Tp;
-    const int tid = threadIdx.x;
-    const int u = slice * blockDim.x + tid;   // 16-byte output unit of the row
+constexpr int kMaxIdsPerThread = 16;   // expert ids a thread of the counting form keeps in registers
 
-    // the row's loads go out first so they overlap the position lookups below
-    uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
+// The token's row, loaded before anything else so its latency overlaps the
+// position work (FP8 reads 32 bytes of bf16 per 16-byte output unit).
+template <bool FP8, bool NTL>
+__device__ __forceinline__ void load_row(const uint4* __restrict__ x, int t, int L, int u, uint4& xa, uint4& xb) {
+    xa = make_uint4(0u, 0u, 0u, 0u);
+    xb = xa;
     if (u < L) {
         if (FP8) {
             xa = ld16<NTL>(&x[(size_t)t * (2 * L) + 2 * u]);
@@ -57,37 +64,40 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
             xa = ld16<NTL>(&x[(size_t)t * L + u]);
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
+}
 
-    if (tid < k) {
-        const int a = t * k + tid;
-        const int e = ids[a];
-        const int br = bucket_rank[a];
-        const int p = send_off[s * E + e] + br;
-        const int q = recv_off[s * E + e] + br;
-        pos[tid] = DIRECT ? q : p;
-        if (slice == 0) {
-            send_pos[a] = p;
-            recv_pos[a] = q;
-            if (!DIRECT) {
-                send_to_recv[p] = q;
-                recv_to_send[q] = p;
-            }
-            HandleRecord m;
-            m.src_rank = s;
-            m.src_token = t - s * Tp;
-            m.slot = (int16_t)tid;
-            m.local_expert = (int16_t)(e % Ep);
-            m.weight = w[a];
-            dst_meta[DIRECT ? q : p] = m;
-        }
+// Handle record, position arrays and (base form) the send <-> receive maps of
+// assignment a = t*k + j; called by the first slice only, after the block's
+// barrier (a barrier waits for the block's outstanding global stores, so stores
+// issued before it would sit on the critical path).
+template <bool DIRECT>
+__device__ __forceinline__ void write_handle(int a, int t, int s, int Tp, int j, int e, int Ep, int p, int q,
+                                             float weight, HandleRecord* __restrict__ dst_meta,
+                                             int32_t* __restrict__ send_to_recv, int32_t* __restrict__ recv_to_send,
+                                             int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos) {
+    send_pos[a] = p;
+    recv_pos[a] = q;
+    if (!DIRECT) {
+        send_to_recv[p] = q;
+        recv_to_send[q] = p;
     }
-    __syncthreads();
+    HandleRecord m;
+    m.src_rank = s;
+    m.src_token = t - s * Tp;
+    m.slot = (int16_t)j;
+    m.local_expert = (int16_t)(e % Ep);
+    m.weight = weight;
+    dst_meta[DIRECT ? q : p] = m;
+}
 
+// The row (or its FP8 form and scales) to the k rows pos[0..k).
+template <bool FP8, bool NTS>
+__device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, const int32_t* pos, int k, int L, int u,
+                                           uint4* __restrict__ dst, float* __restrict__ dst_scales) {
+    if (u >= L) return;
     if (FP8) {
         // lanes u..u+7 share a 128-channel block; L % 8 == 0 and blocks start at
         // multiples of 64 lanes, so a block's lanes are all valid or all not
-        if (u >= L) return;
         float f[16];
         {
             float lo[8], hi[8];
@@ -111,7 +121,23 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) q[w4] |= ((__float_as_uint(f[4 * w4 + i]) >> 24) & 0x80u) << (8 * i);
             }
-        } else {
+        } else if (amax >= 0x1p-64f && amax < __builtin_inff()) {
+            // x / scale through the reciprocal: q0 = x * r, then one correction with the
+            // exact remainder x - q0 * scale (an FMA).  The corrected quotient can be one
+            // ulp off the correctly rounded one, but never across an E4M3 rounding
+            // boundary: checked for every bf16 amax >= 2^-64 and every bf16 |x| <= amax
+            // (the remainder stays far from underflow there).  Three operations per
+            // channel instead of a full division.
+            const float r = 1.0f / scale;
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float q0 = f[i] * r;
+                v[i] = fmaf(fmaf(-q0, scale, f[i]), r, q0);
+            }
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) q[w4] = pack4_e4m3(v[4 * w4], v[4 * w4 + 1], v[4 * w4 + 2], v[4 * w4 + 3]);
+        } else {                                  // tiny blocks: correctly rounded division
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4)
                 q[w4] = pack4_e4m3(f[4 * w4] / scale, f[4 * w4 + 1] / scale, f[4 * w4 + 2] / scale,
@@ -125,12 +151,227 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
             if ((u & 7) == 0) dst_scales[(size_t)p * nb + (u >> 3)] = scale;
         }
     } else {
-        if (u >= L) return;
         for (int j = 0; j < k; ++j) st16<NTS>(&dst[(size_t)pos[j] * L + u], xa);
     }
 }
 
+template <bool FP8, bool NTL = false, bool NTS = false, bool DIRECT = false>
+__global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
+                                                   const float* __restrict__ w,
+                                                   const int32_t* __restrict__ bucket_rank,
+                                                   const int32_t* __restrict__ send_off,
+                                                   const int32_t* __restrict__ recv_off,
+                                                   uint4* __restrict__ dst, float* __restrict__ dst_scales,
+                                                   HandleRecord* __restrict__ dst_meta, int32_t* __restrict__ send_to_recv,
+                                                   int32_t* __restrict__ recv_to_send,
+                                                   int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
+                                                   int Tp, int E, int Ep, int k, int L) {
+    __shared__ int32_t pos[32];
+    const int t = blockIdx.x;
+    const int slice = blockIdx.y;
+    const int s = t / Tp;
+    const int tid = threadIdx.x;
+    const int u = slice * blockDim.x + tid;   // 16-byte output unit of the row
+
+    uint4 xa, xb;
+    load_row<FP8, NTL>(x, t, L, u, xa, xb);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int a = t * k + tid;
+    int e = 0, p = 0, q = 0;
+    float wt = 0.0f;
+    if (tid < k) {
+        e = ids[a];
+        const int br = bucket_rank[a];
+        wt = w[a];
+        p = send_off[s * E + e] + br;
+        q = recv_off[s * E + e] + br;
+        pos[tid] = DIRECT ? q : p;
+    }
+    __syncthreads();
+    store_rows<FP8, NTS>(xa, xb, pos, k, L, u, dst, dst_scales);
+    if (tid < k && slice == 0)
+        write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send, send_pos,
+                             recv_pos);
+}
+
+// Counts and offsets of source rank s for the handle (one workgroup of the
+// counting form per rank): LDS histograms of all ids, of the ids of ranks
+// below s and of rank s's ids, then exclusive scans over the experts.
+__device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int E, int Ep, int k, int P, int Na,
+                            int32_t* __restrict__ n, int32_t* __restrict__ N, int32_t* __restrict__ C,
+                            int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_recv_off,
+                            int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off) {
+    extern __shared__ __align__(16) int32_t hist[];   // [3][E]: all ranks, ranks < s, rank s
+    __shared__ int32_t tmp[17];
+    int32_t* h_all = hist;
+    int32_t* h_lo = hist + E;
+    int32_t* h_s = hist + 2 * E;
+    const int tid = threadIdx.x, bs = blockDim.x;
+    const int lo = s * Tp * k, hi = lo + Tp * k;   // rank s's assignments
+    int id[kMaxIdsPerThread];                    // all loads in flight at once (Na <= kMaxIdsPerThread * bs)
+#pragma unroll
+    for (int m = 0; m < kMaxIdsPerThread; ++m) {
+        const int a = tid + m * bs;
+        id[m] = a < Na ? ids[a] : -1;
+    }
+    for (int x = tid; x < 3 * E; x += bs) hist[x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kMaxIdsPerThread; ++m) {
+        const int a = tid + m * bs;
+        const int e = id[m];
+        if ((unsigned)e >= (unsigned)E) continue;   // padding; out-of-range ids are outside the contract, never indexed
+        atomicAdd(&h_all[e], 1);
+        if (a < lo) atomicAdd(&h_lo[e], 1);
+        else if (a < hi) atomicAdd(&h_s[e], 1);
+    }
+    __syncthreads();
+    for (int r = tid; r < P; r += bs) {
+        int c = 0;
+        for (int e = r * Ep; e < (r + 1) * Ep; ++e) c += h_s[e];
+        C[(size_t)s * P + r] = c;
+    }
+    int carry_all = 0, carry_s = 0;
+    for (int e0 = 0; e0 < E; e0 += bs) {          // uniform loop: every thread calls the scans
+        const int e = e0 + tid;
+        const int ca = e < E ? h_all[e] : 0;
+        const int cs = e < E ? h_s[e] : 0;
+        int tot_a, tot_s;
+        const int xa = block_exclusive_scan(ca, tmp, &tot_a);
+        const int xs = block_exclusive_scan(cs, tmp, &tot_s);
+        if (e < E) {
+            const int eo = carry_all + xa;
+            n[(size_t)s * E + e] = cs;
+            send_off[(size_t)s * E + e] = lo + carry_s + xs;
+            recv_off[(size_t)s * E + e] = eo + h_lo[e];
+            if (s == 0) {
+                N[e] = ca;
+                expert_off[e] = eo;
+                if (e % Ep == 0) rank_recv_off[e / Ep] = eo;
+            }
+        }
+        carry_all += tot_a;
+        carry_s += tot_s;
+    }
+    if (s == 0 && tid == 0) {
+        expert_off[E] = carry_all;
+        rank_recv_off[P] = carry_all;
+    }
+}
+
+// Grid (P + T, slices): block s < P of slice 0 writes rank s's counts and
+// offsets (the other slices of those blocks exit); block P + t packs token t.
+// The counting blocks come first so they run alongside the packing ones.
+template <bool FP8, bool DIRECT, int MI>
+__global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ w, uint4* __restrict__ dst,
+                                                         float* __restrict__ dst_scales,
+                                                         HandleRecord* __restrict__ dst_meta,
+                                                         int32_t* __restrict__ send_to_recv,
+                                                         int32_t* __restrict__ recv_to_send,
+                                                         int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
+                                                         int32_t* __restrict__ n, int32_t* __restrict__ N,
+                                                         int32_t* __restrict__ C, int32_t* __restrict__ expert_off,
+                                                         int32_t* __restrict__ rank_recv_off,
+                                                         int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off,
+                                                         int T, int Tp, int E, int Ep, int k, int P, int L) {
+    __shared__ int32_t pos[32];
+    __shared__ int32_t red[32][8];             // per-slot wave partial counts; <= 8 waves
+    const int slice = blockIdx.y;
+    const int tid = threadIdx.x, bs = blockDim.x;
+    const int Na = T * k;
+    if ((int)blockIdx.x < P) {
+        if (slice == 0)
+            rank_counts(ids, blockIdx.x, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off, recv_off);
+        return;
+    }
+    const int t = blockIdx.x - P;
+    const int s = t / Tp;
+    const int u = slice * bs + tid;
+
+    // the ids first (coalesced, all in flight at once), then the token's row: the
+    // counting below waits for the ids only, and LDS-only barriers keep the row's
+    // loads in flight until the rows are stored
+    // (MI ids per thread, MI * blockDim.x >= N_a; straight-line code with clamped
+    // addresses, so the waits for the ids do not also wait for the row)
+    extern __shared__ __align__(16) int32_t staged[];   // [MI * blockDim.x], ids beyond N_a unused
+    int raw[MI];
+#pragma unroll
+    for (int m = 0; m < MI; ++m) raw[m] = ids[min(tid + m * bs, Na - 1)];
+    const float wt = w[t * k + min(tid, k - 1)];   // used by threads < k
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 xa, xb;
+    load_row<FP8, false>(x, t, L, u, xa, xb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < MI; ++m) staged[tid + m * bs] = raw[m];
+    lds_barrier();
+
+    // lane (j, sub) of a wave counts, for slot j = lane mod kp, the ids of its run of
+    // the wave's share: receive count in the low half, same-rank count in the high
+    // half of one word (each is below N_a <= 8192); an xor butterfly over the g
+    // lanes of a slot then sums the wave's runs
+    const int tk = t * k, lo = s * Tp * k, hi = lo + Tp * k;
+    const int lane = tid & (kWave - 1), wave = tid / kWave, nw = bs / kWave;
+    int kp = 1;
+    while (kp < k) kp <<= 1;                   // k <= 32, so g >= 2 lanes per slot
+    const int g = kWave / kp;
+    const int j = lane & (kp - 1), sub = lane / kp;
+    const int per_wave = (Na + nw - 1) / nw;
+    const int chunk = (per_wave + 4 * g - 1) / (4 * g) * (4 * g);
+    const int run = chunk / g;                 // a multiple of 4: 16-byte LDS reads stay aligned
+    const int base = wave * chunk + sub * run;
+    const int thr = j < k ? (int)(2u * (unsigned)staged[tk + j] + 1u) : (int)0x80000000;   // padding slots count nothing
+    int c = 0;
+    for (int i = 0; i < run; i += 4) {
+        const int a0 = base + i;
+        if (a0 >= Na) break;
+        const int4 v = *reinterpret_cast<const int4*>(&staged[a0]);
+        const int vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int a = a0 + e4;
+            const int key = (int)(2u * (unsigned)vv[e4] + (a >= tk ? 1u : 0u));
+            if (a < Na && key < thr) c += (a >= lo && a < hi) ? 0x10001 : 1;
+        }
+    }
+    for (int mask = kp; mask < kWave; mask <<= 1) c += __shfl_xor(c, mask);
+    if (sub == 0 && j < k) red[j][wave] = c;
+    lds_barrier();
+    int p = 0, q = 0;
+    if (tid < k) {
+        int c = 0;
+        for (int v = 0; v < nw; ++v) c += red[tid][v];
+        q = c & 0xFFFF;
+        p = lo + (c >> 16);
+        pos[tid] = DIRECT ? q : p;
+    }
+    lds_barrier();
+    store_rows<FP8, false>(xa, xb, pos, k, L, u, dst, dst_scales);
+    if (tid < k && slice == 0)
+        write_handle<DIRECT>(tk + tid, t, s, Tp, tid, staged[tk + tid], Ep, p, q, wt, dst_meta, send_to_recv,
+                             recv_to_send, send_pos, recv_pos);
+}
+
 }  // namespace
+
+// Ids per thread of the counting form's staging loop: 4, 8 or 16.
+int staging_ids_per_thread(long long Na, int B) {
+    const long long m = (Na + B - 1) / B;
+    return m <= 4 ? 4 : m <= 8 ? 8 : 16;
+}
+
+bool pack_counts(const Dims& d) {
+    if (d.T == 0 || d.count_path == CountPath::kSeparate) return false;
+    const int B = pick_block(d.row_units);
+    const long long blocks = (long long)d.T * ((d.row_units + B - 1) / B);
+    // every thread keeps its share of the ids in registers, and the ids all
+    // workgroups read together stay small (measured on gfx950: a win at 128
+    // tokens x top-8, 256 workgroups; a loss at 2048 tokens x top-2 with 2048
+    // workgroups reading 4096 ids each, where the count launch is cheaper)
+    return d.Na <= (long long)kMaxIdsPerThread * B && blocks * d.Na <= (1LL << 21);
+}
 
 hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w, const Workspace& ws,
                        void* dst, float* dst_scales, bool direct, hipStream_t st) {
@@ -138,6 +379,24 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     const int L = d.row_units;                 // 16-byte output units per dispatched row
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
+    HandleRecord* meta = reinterpret_cast<HandleRecord*>(direct ? ws.recv_meta : ws.send_meta);
+    if (pack_counts(d)) {
+        const int mi = staging_ids_per_thread(d.Na, B);
+        auto pick = [&](auto fp8, auto dir) {
+            constexpr bool F = decltype(fp8)::value, D = decltype(dir)::value;
+            return mi == 4 ? count_pack_kernel<F, D, 4> : mi == 8 ? count_pack_kernel<F, D, 8> : count_pack_kernel<F, D, 16>;
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
+        const size_t lds = 4 * std::max<size_t>(3 * (size_t)d.E, (size_t)mi * B);   // histograms | staged ids
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(d.P + d.T), (unsigned)slices), dim3(B), lds, st,
+                           reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
+                           ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
+                           ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
+                           L);
+        return hipGetLastError();
+    }
     const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = pack_kernel<false, false, false, false>;
     if (d.fp8) {
@@ -149,9 +408,8 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     }
     hipLaunchKernelGGL(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
-                       reinterpret_cast<uint4*>(dst), dst_scales,
-                       reinterpret_cast<HandleRecord*>(direct ? ws.recv_meta : ws.send_meta), ws.send_to_recv,
-                       ws.recv_to_send, ws.send_pos, ws.recv_pos, d.Tp, d.E, d.Ep, d.P, d.k, L, slices);
+                       reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
+                       ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L);
     return hipGetLastError();
 }
 

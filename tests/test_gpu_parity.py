@@ -62,6 +62,17 @@ def test_workload_parity_other_cache_policy(orc, monkeypatch, policy, name):
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {policy}")
 
 
+@pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True)])
+def test_workload_parity_separate_count(orc, monkeypatch, name, direct):
+    # small problems rank their assignments inside the pack kernel; force the
+    # count (and scan) kernels on the same data
+    monkeypatch.setenv("MOE_EP_COUNT_PATH", "separate")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} separate count",
+                 direct=direct)
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_workload_parity_direct(orc, name):
     # pack straight into the receive rows, reduce straight from the expert output
@@ -151,14 +162,17 @@ EDGE = [
     ("k-equals-E", 2, 9, 4, 4, 128, True),
     ("count-chunks-Tp3000", 2, 3000, 256, 8, 64, False),
     ("E1024-top32", 4, 40, 1024, 32, 128, True),
+    ("E1024-top32-wide-rows", 4, 4, 1024, 32, 7168, False),
     ("E-odd-96", 3, 50, 96, 5, 520, False),
 ]
 
 
-@pytest.mark.parametrize("policy,direct", [("auto", False), ("streaming", False), ("auto", True)])
+@pytest.mark.parametrize("policy,count,direct", [("auto", "auto", False), ("streaming", "auto", False),
+                                                 ("auto", "auto", True), ("auto", "separate", False)])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, direct):
+def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, count, direct):
     monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
+    monkeypatch.setenv("MOE_EP_COUNT_PATH", count)
     sh = orc.Shape(P, P * Tp, E, k, H, fp8)
     seed = zlib.crc32(name.encode())
     x = wl.make_hidden(seed, sh.T, H)
@@ -209,6 +223,14 @@ def test_fp8_special_blocks(orc):
     x[1, 255] = wl.float32_to_bf16_bits(np.float32([448.0]))[0]
     x[2, 256:384] = wl.float32_to_bf16_bits(np.full(128, 1e-30, np.float32))
     x[3, 384:512] = wl.float32_to_bf16_bits(np.linspace(-3e38, 3e38, 128).astype(np.float32))
+    # both sides of amax = 2^-64, where the kernel switches between the reciprocal
+    # and the divided quotient, and bf16 subnormals under a large amax
+    g = np.random.default_rng(7).standard_normal(128).astype(np.float32)
+    x[4, 0:128] = wl.float32_to_bf16_bits(g / np.abs(g).max() * np.float32(2.0 ** -64))
+    x[5, 128:256] = wl.float32_to_bf16_bits(g / np.abs(g).max() * np.float32(2.0 ** -64 * (1 - 2 ** -7)))
+    x[6, 256:384] = (np.arange(128, dtype=np.uint16) % 0x80) | np.where(np.arange(128) % 2, 0x8000, 0).astype(np.uint16)
+    x[6, 300] = wl.float32_to_bf16_bits(np.float32([1e30]))[0]
+    x[7, 384:512] = (np.arange(128, dtype=np.uint16) % 0x80)
     logits = wl.make_logits(6, T, E)
     _full_parity(orc, sh, x, logits=logits, label="fp8 special blocks")
 
