@@ -98,14 +98,23 @@ def load_traffic(config: str, kernel: str):
 
 KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the path
     ("route_topk", "route_topk"), ("count_scan_single_kernel", "count"), ("count_kernel", "count"),
-    ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"), ("reverse_exchange_kernel", "reverse_exchange"),
+    ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"), ("reverse_exchange_", "reverse_exchange"),
     ("exchange_kernel", "exchange"), ("stub_kernel", "stub"), ("reduce_kernel", "reduce"),
 )
+
+
+# template argument that marks the direct form: position in the argument list
+DIRECT_TEMPLATE_ARG = {"count_pack": 1, "pack": 3, "reduce": 2}
 
 
 def path_kernel(rocprof_name: str):
     for frag, k in KERNEL_NAME_PATTERNS:
         if frag in rocprof_name:
+            i = DIRECT_TEMPLATE_ARG.get(k)
+            if i is not None:
+                args = rocprof_name.split(frag + "<", 1)[1].split(">", 1)[0].split(",")
+                if args[i].strip() == "true":
+                    k += "_direct"
             return k
     return None
 

@@ -58,24 +58,22 @@ hipEvent_t take_event(moe_ctx* ctx) {
     return e;
 }
 
-// Launches one kernel through `fn`, bracketed by events when timing is on.
+// Launches one kernel through `fn`; when timing is on, the launch carries a
+// start and a stop event that bracket the kernel's execution.
 template <typename Fn>
 moe_status launch(moe_ctx* ctx, const char* name, hipStream_t st, Fn&& fn) {
+    (void)st;
     hipEvent_t a = nullptr, b = nullptr;
     if (ctx->timing) {
         a = take_event(ctx);
         b = take_event(ctx);
         if (!a || !b) return hip_fail(hipErrorOutOfMemory, "hipEventCreate");
-        hipError_t e = hipEventRecord(a, st);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
+    moe::launch_timing = {a, b};
     hipError_t e = fn();
+    moe::launch_timing = {};
     if (e != hipSuccess) return hip_fail(e, name);
-    if (ctx->timing) {
-        e = hipEventRecord(b, st);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-        ctx->records.push_back({name, a, b});
-    }
+    if (ctx->timing) ctx->records.push_back({name, a, b});
     return MOE_OK;
 }
 
@@ -200,10 +198,12 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
         if (std::strcmp(pol, "temporal") == 0) d.policy = moe::CachePolicy::kTemporal;
         if (std::strcmp(pol, "streaming") == 0) d.policy = moe::CachePolicy::kStreaming;
     }
-    // MOE_EP_COUNT_PATH=separate keeps the count kernels for small problems too (for A/B tests)
+    // MOE_EP_COUNT_PATH=separate|fused overrides the size-based choice (for A/B tests)
     d.count_path = moe::CountPath::kAuto;
-    if (const char* cp = std::getenv("MOE_EP_COUNT_PATH"))
+    if (const char* cp = std::getenv("MOE_EP_COUNT_PATH")) {
         if (std::strcmp(cp, "separate") == 0) d.count_path = moe::CountPath::kSeparate;
+        if (std::strcmp(cp, "fused") == 0) d.count_path = moe::CountPath::kFused;
+    }
 
     const size_t P = d.P, E = d.E, tk = (size_t)Na;
     size_t off = 0;

@@ -104,23 +104,23 @@ __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t* __restri
             myid[j] = a < na ? rank_ids[(size_t)c0 * k + a] : 0;
         }
         for (int x = tid; x < EW; x += bs) bitmap[x] = 0;
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < kMaxPerThread; ++j) {
             const int a = tid + j * bs;
             if (a < na) atomicOr(&bitmap[myid[j] * W + ((a / k) >> 5)], 1u << ((a / k) & 31));
         }
-        __syncthreads();
+        lds_barrier();
         segmented_word_prefix(bitmap, prefix, EW, W);
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < kMaxPerThread; ++j) {
             const int a = tid + j * bs;
             if (a < na) rank_br[(size_t)c0 * k + a] = carry[myid[j]] + bucket_rank_of(bitmap, prefix, myid[j], W, a / k);
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < E; e += bs) carry[e] += word_total(bitmap, prefix, e, W);
-        __syncthreads();
+        lds_barrier();
     }
 
     // counts and send offsets: bucket (s, e) follows rank s's buckets of lower
@@ -162,7 +162,7 @@ __device__ void cross_rank_scan(const int32_t* n, int P, int E, int Ep, int32_t*
         expert_off[E] = total;
         off[E] = total;
     }
-    __syncthreads();
+    lds_barrier();
     for (int r = threadIdx.x; r <= P; r += blockDim.x) rank_recv_off[r] = off[r * Ep];
 }
 
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
                 if (x < total) nl[x] = v[j];
             }
         }
-        __syncthreads();
+        lds_barrier();
         src = nl;
     }
     cross_rank_scan(src, P, E, Ep, off, tmp, N, expert_off, recv_off, rank_recv_off);
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void count_scan_single_kernel(
         myid[j] = a < Na ? ids[a] : 0;
     }
     for (int x = tid; x < PE * W; x += bs) bitmap[x] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j) {
         const int a = tid + j * bs;
@@ -232,10 +232,10 @@ __global__ __launch_bounds__(kThreads) void count_scan_single_kernel(
             atomicOr(&bitmap[(s * E + myid[j]) * W + (i >> 5)], 1u << (i & 31));
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (W > 1) {
         segmented_word_prefix(bitmap, prefix, PE * W, W);
-        __syncthreads();
+        lds_barrier();
     } else {
         for (int x = tid; x < PE; x += bs) prefix[x] = 0;
     }
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void count_scan_single_kernel(
         nl[x] = c;
         n_out[x] = c;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j) {
         const int a = tid + j * bs;
@@ -294,7 +294,7 @@ bool count_is_single(const Dims& d) {
 hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, hipStream_t st) {
     if (count_is_single(d)) {
         const int W = single_words(d);
-        hipLaunchKernelGGL(count_scan_single_kernel, dim3(1), dim3(kThreads), single_lds_bytes(d.P, d.E, W), st, ids,
+        launch_kernel(count_scan_single_kernel, dim3(1), dim3(kThreads), single_lds_bytes(d.P, d.E, W), st, ids,
                            d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n, ws.send_off, ws.C, ws.bucket_rank, ws.N,
                            ws.expert_off, ws.recv_off, ws.rank_recv_off);
         return hipGetLastError();
@@ -302,7 +302,7 @@ hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, 
     int W = words_per_expert(d.E, d.Tp, 48 * 1024);
     while (W > 1 && 32LL * W * d.k > (long long)kMaxPerThread * kThreads) W /= 2;
     const size_t lds = (2 * (size_t)d.E * W + d.E) * 4;
-    hipLaunchKernelGGL(count_kernel, dim3(d.P), dim3(kThreads), lds, st, ids, d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n,
+    launch_kernel(count_kernel, dim3(d.P), dim3(kThreads), lds, st, ids, d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n,
                        ws.send_off, ws.C, ws.bucket_rank);
     return hipGetLastError();
 }
@@ -310,7 +310,7 @@ hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, 
 hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st) {
     const bool stage = ((size_t)d.P * d.E + d.E + 1) * 4 <= kLdsBudget;
     const size_t lds = stage ? ((size_t)d.P * d.E + d.E + 1) * 4 : ((size_t)d.E + 1) * 4;
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), lds, st, ws.n, d.P, d.E, d.Ep, stage ? 1 : 0, ws.N,
+    launch_kernel(scan_kernel, dim3(1), dim3(kThreads), lds, st, ws.n, d.P, d.E, d.Ep, stage ? 1 : 0, ws.N,
                        ws.expert_off, ws.recv_off, ws.rank_recv_off);
     return hipGetLastError();
 }

@@ -146,17 +146,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
     const int nw = blockDim.x / kWave;
     const int incl = wave_inclusive_scan(v);
     if (lane == kWave - 1) tmp[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         int w = lane < nw ? tmp[lane] : 0;
         const int wincl = wave_inclusive_scan(w);
         if (lane < nw) tmp[lane] = wincl - w;
         if (lane == nw - 1) tmp[nw] = wincl;
     }
-    __syncthreads();
+    lds_barrier();
     const int out = tmp[wave] + incl - v;
     if (total) *total = tmp[nw];
-    __syncthreads();
+    lds_barrier();
     return out;
 }
 

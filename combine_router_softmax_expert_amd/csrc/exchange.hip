@@ -88,7 +88,7 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int slices = (L + B - 1) / B;
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
+    launch_kernel(kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
                        gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
                        reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L,
@@ -103,11 +103,11 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (streaming(d, 2LL * d.Na * 16LL * L))
-        hipLaunchKernelGGL(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
+        launch_kernel(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                            reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
                            slices);
     else
-        hipLaunchKernelGGL(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
+        launch_kernel(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                            reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
                            reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
     return hipGetLastError();

@@ -1,10 +1,26 @@
 // kernels.hpp -- host launchers of the gfx950 kernels (internal to libmoe_ep.so).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Events the next kernel launch of this thread records at its start and end
+// (set by the library while it times kernels; null otherwise).  The events
+// travel in the dispatch itself, so they bracket the kernel alone, not the
+// gaps between launches.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline thread_local LaunchTiming launch_timing;
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds_bytes, hipStream_t st, Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds_bytes, st, launch_timing.start, launch_timing.stop, 0u,
+                          args...);
+}
 
 // The 16-byte handle record that travels with every dispatched row (the ABI's moe_meta).
 struct HandleRecord {
@@ -23,8 +39,9 @@ constexpr long long kStreamingBytes = 128LL << 20;
 
 // How dispatch ranks the assignments: kAuto lets the pack kernel count by itself
 // when the problem is small enough (pack_counts), kSeparate always launches the
-// count (and scan) kernels first.
-enum class CountPath { kAuto = 0, kSeparate = 1 };
+// count (and scan) kernels first, kFused counts in the pack kernel whenever its
+// staging fits.
+enum class CountPath { kAuto = 0, kSeparate = 1, kFused = 2 };
 
 struct Dims {
     int P, Tp, T, E, Ep, k, H;

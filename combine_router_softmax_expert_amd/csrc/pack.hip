@@ -188,7 +188,7 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
         q = recv_off[s * E + e] + br;
         pos[tid] = DIRECT ? q : p;
     }
-    __syncthreads();
+    lds_barrier();
     store_rows<FP8, NTS>(xa, xb, pos, k, L, u, dst, dst_scales);
     if (tid < k && slice == 0)
         write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send, send_pos,
@@ -216,7 +216,7 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
         id[m] = a < Na ? ids[a] : -1;
     }
     for (int x = tid; x < 3 * E; x += bs) hist[x] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < kMaxIdsPerThread; ++m) {
         const int a = tid + m * bs;
@@ -226,7 +226,7 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
         if (a < lo) atomicAdd(&h_lo[e], 1);
         else if (a < hi) atomicAdd(&h_s[e], 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int r = tid; r < P; r += bs) {
         int c = 0;
         for (int e = r * Ep; e < (r + 1) * Ep; ++e) c += h_s[e];
@@ -366,11 +366,12 @@ bool pack_counts(const Dims& d) {
     if (d.T == 0 || d.count_path == CountPath::kSeparate) return false;
     const int B = pick_block(d.row_units);
     const long long blocks = (long long)d.T * ((d.row_units + B - 1) / B);
-    // every thread keeps its share of the ids in registers, and the ids all
-    // workgroups read together stay small (measured on gfx950: a win at 128
-    // tokens x top-8, 256 workgroups; a loss at 2048 tokens x top-2 with 2048
-    // workgroups reading 4096 ids each, where the count launch is cheaper)
-    return d.Na <= (long long)kMaxIdsPerThread * B && blocks * d.Na <= (1LL << 21);
+    // every thread stages at most kMaxIdsPerThread ids, and the ids all workgroups
+    // read together stay well below the payload (measured on gfx950: a win at
+    // 128 tokens x top-8 with 256 workgroups and at 2048 tokens x top-2 with 2048
+    // workgroups staging 4096 ids each)
+    if (d.Na > (long long)kMaxIdsPerThread * B) return false;
+    return d.count_path == CountPath::kFused || blocks * d.Na <= (1LL << 24);
 }
 
 hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w, const Workspace& ws,
@@ -390,7 +391,7 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         using F_ = std::false_type;
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
         const size_t lds = 4 * std::max<size_t>(3 * (size_t)d.E, (size_t)mi * B);   // histograms | staged ids
-        hipLaunchKernelGGL(kernel, dim3((unsigned)(d.P + d.T), (unsigned)slices), dim3(B), lds, st,
+        launch_kernel(kernel, dim3((unsigned)(d.P + d.T), (unsigned)slices), dim3(B), lds, st,
                            reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
                            ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
                            ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
@@ -406,7 +407,7 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         if (direct) kernel = nt ? pack_kernel<false, true, false, true> : pack_kernel<false, false, false, true>;
         else kernel = nt ? pack_kernel<false, true, false, false> : pack_kernel<false, false, false, false>;
     }
-    hipLaunchKernelGGL(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
+    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
                        reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
                        ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L);

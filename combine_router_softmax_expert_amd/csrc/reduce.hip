@@ -64,7 +64,7 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
     const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
     auto kernel = direct ? (nt ? reduce_kernel<true, true, true> : reduce_kernel<false, false, true>)
                          : (nt ? reduce_kernel<true, true, false> : reduce_kernel<false, false, false>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
+    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
                        reinterpret_cast<const uint4*>(rows), recv_pos, w, reinterpret_cast<uint4*>(y), d.k, L);
     return hipGetLastError();
 }

@@ -147,7 +147,7 @@ hipError_t launch_rtw(const Dims& d, const float* logits, int32_t* ids, float* w
     constexpr int kThreads = 256;
     const int tokens_per_block = kThreads / kWave;
     const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
-    hipLaunchKernelGGL((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
+    launch_kernel((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
                        d.k);
     return hipGetLastError();
 }
@@ -157,7 +157,7 @@ hipError_t launch_rt(const Dims& d, const float* logits, int32_t* ids, float* w,
     constexpr int kThreads = 256;
     const int tokens_per_block = (kThreads / kWave) * (kWave / G);
     const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
-    hipLaunchKernelGGL((route_topk_kernel<G, V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w,
+    launch_kernel((route_topk_kernel<G, V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w,
                        d.T, d.E, d.k);
     return hipGetLastError();
 }

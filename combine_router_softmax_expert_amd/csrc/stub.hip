@@ -86,7 +86,7 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     // streaming: e4m3 rows load nontemporally, bf16 rows store nontemporally (best of the four choices each)
     auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, false> : stub_kernel<true, false, false>)
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
-    hipLaunchKernelGGL(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+    launch_kernel(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
                        reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
                        d.P, d.E, d.Ep, L, slices);
     return hipGetLastError();

@@ -62,7 +62,7 @@ def test_workload_parity_other_cache_policy(orc, monkeypatch, policy, name):
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {policy}")
 
 
-@pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True)])
+@pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True), ("c3", False)])
 def test_workload_parity_separate_count(orc, monkeypatch, name, direct):
     # small problems rank their assignments inside the pack kernel; force the
     # count (and scan) kernels on the same data
