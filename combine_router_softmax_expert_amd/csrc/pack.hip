@@ -260,10 +260,12 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
     }
 }
 
-// Grid (P + T, slices): block s < P of slice 0 writes rank s's counts and
-// offsets (the other slices of those blocks exit); block P + t packs token t.
-// The counting blocks come first so they run alongside the packing ones.
-template <bool FP8, bool DIRECT, int MI>
+// Grid (P + ceil(T / TPB), slices): block s < P of slice 0 writes rank s's
+// counts and offsets (the other slices of those blocks exit); block P + b packs
+// tokens b*TPB .. b*TPB + TPB - 1, whose TPB * k <= 32 assignments ("slots")
+// share one staging and counting pass.  The counting blocks come first so they
+// run alongside the packing ones.
+template <bool FP8, bool DIRECT, int MI, int TPB>
 __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
                                                          const float* __restrict__ w, uint4* __restrict__ dst,
                                                          float* __restrict__ dst_scales,
@@ -286,43 +288,48 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
             rank_counts(ids, blockIdx.x, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off, recv_off);
         return;
     }
-    const int t = blockIdx.x - P;
-    const int s = t / Tp;
+    const int t0 = ((int)blockIdx.x - P) * TPB;
+    const int ntok = min(TPB, T - t0);
+    const int nslots = ntok * k;               // <= 32 by the launch condition
     const int u = slice * bs + tid;
 
-    // the ids first (coalesced, all in flight at once), then the token's row: the
-    // counting below waits for the ids only, and LDS-only barriers keep the row's
+    // the ids first (coalesced, all in flight at once), then the tokens' rows: the
+    // counting below waits for the ids only, and LDS-only barriers keep the rows'
     // loads in flight until the rows are stored
     // (MI ids per thread, MI * blockDim.x >= N_a; straight-line code with clamped
-    // addresses, so the waits for the ids do not also wait for the row)
+    // addresses, so the waits for the ids do not also wait for the rows)
     extern __shared__ __align__(16) int32_t staged[];   // [MI * blockDim.x], ids beyond N_a unused
     int raw[MI];
 #pragma unroll
     for (int m = 0; m < MI; ++m) raw[m] = ids[min(tid + m * bs, Na - 1)];
-    const float wt = w[t * k + min(tid, k - 1)];   // used by threads < k
+    const float wt = w[t0 * k + min(tid, nslots - 1)];   // used by threads < nslots
     __builtin_amdgcn_sched_barrier(0);
-    uint4 xa, xb;
-    load_row<FP8, false>(x, t, L, u, xa, xb);
+    uint4 xa[TPB], xb[TPB];
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) load_row<FP8, false>(x, min(t0 + i, T - 1), L, u, xa[i], xb[i]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < MI; ++m) staged[tid + m * bs] = raw[m];
     lds_barrier();
 
-    // lane (j, sub) of a wave counts, for slot j = lane mod kp, the ids of its run of
-    // the wave's share: receive count in the low half, same-rank count in the high
-    // half of one word (each is below N_a <= 8192); an xor butterfly over the g
-    // lanes of a slot then sums the wave's runs
-    const int tk = t * k, lo = s * Tp * k, hi = lo + Tp * k;
+    // lane (sl, sub) of a wave counts, for slot sl = lane mod kp (token t0 + sl / k,
+    // top-k slot sl % k), the ids of its run of the wave's share: receive count in
+    // the low half, same-rank count in the high half of one word (each is below
+    // N_a <= 8192); an xor butterfly over the g lanes of a slot then sums the
+    // wave's runs
     const int lane = tid & (kWave - 1), wave = tid / kWave, nw = bs / kWave;
     int kp = 1;
-    while (kp < k) kp <<= 1;                   // k <= 32, so g >= 2 lanes per slot
+    while (kp < nslots) kp <<= 1;              // nslots <= 32, so g >= 2 lanes per slot
     const int g = kWave / kp;
-    const int j = lane & (kp - 1), sub = lane / kp;
+    const int sl = lane & (kp - 1), sub = lane / kp;
     const int per_wave = (Na + nw - 1) / nw;
     const int chunk = (per_wave + 4 * g - 1) / (4 * g) * (4 * g);
     const int run = chunk / g;                 // a multiple of 4: 16-byte LDS reads stay aligned
     const int base = wave * chunk + sub * run;
-    const int thr = j < k ? (int)(2u * (unsigned)staged[tk + j] + 1u) : (int)0x80000000;   // padding slots count nothing
+    const int my_slot = min(sl, nslots - 1);
+    const int tk = t0 * k + my_slot - my_slot % k;   // first assignment of this slot's token
+    const int lo = (tk / k) / Tp * Tp * k, hi = lo + Tp * k;   // its rank's assignments
+    const int thr = sl < nslots ? (int)(2u * (unsigned)staged[t0 * k + sl] + 1u) : (int)0x80000000;   // padding counts nothing
     int c = 0;
     for (int i = 0; i < run; i += 4) {
         const int a0 = base + i;
@@ -337,21 +344,26 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
         }
     }
     for (int mask = kp; mask < kWave; mask <<= 1) c += __shfl_xor(c, mask);
-    if (sub == 0 && j < k) red[j][wave] = c;
+    if (sub == 0 && sl < nslots) red[sl][wave] = c;
     lds_barrier();
     int p = 0, q = 0;
-    if (tid < k) {
+    if (tid < nslots) {
         int c = 0;
         for (int v = 0; v < nw; ++v) c += red[tid][v];
+        const int t = t0 + tid / k;
         q = c & 0xFFFF;
-        p = lo + (c >> 16);
+        p = t / Tp * Tp * k + (c >> 16);
         pos[tid] = DIRECT ? q : p;
     }
     lds_barrier();
-    store_rows<FP8, false>(xa, xb, pos, k, L, u, dst, dst_scales);
-    if (tid < k && slice == 0)
-        write_handle<DIRECT>(tk + tid, t, s, Tp, tid, staged[tk + tid], Ep, p, q, wt, dst_meta, send_to_recv,
-                             recv_to_send, send_pos, recv_pos);
+#pragma unroll
+    for (int i = 0; i < TPB; ++i)
+        if (i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
+    if (tid < nslots && slice == 0) {
+        const int t = t0 + tid / k;
+        write_handle<DIRECT>(t0 * k + tid, t, t / Tp, Tp, tid % k, staged[t0 * k + tid], Ep, p, q, wt, dst_meta,
+                             send_to_recv, recv_to_send, send_pos, recv_pos);
+    }
 }
 
 }  // namespace
@@ -360,6 +372,18 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
 int staging_ids_per_thread(long long Na, int B) {
     const long long m = (Na + B - 1) / B;
     return m <= 4 ? 4 : m <= 8 ? 8 : 16;
+}
+
+// Tokens per workgroup of the counting form: more tokens share one staging and
+// counting pass, as long as their slots fit one wave's lanes (TPB * k <= 32) and
+// at least 1024 workgroups remain (measured on gfx950 at 2048 tokens x top-2:
+// 2 tokens per workgroup 17.8 us, 1 token 20.7 us, 4 tokens 20.0 us).
+int tokens_per_block(const Dims& d) {
+    const int B = pick_block(d.row_units);
+    const long long slices = (d.row_units + B - 1) / B;
+    for (int tpb = 4; tpb > 1; tpb /= 2)
+        if (tpb * d.k <= 32 && (long long)(d.T / tpb) * slices >= 1024) return tpb;
+    return 1;
 }
 
 bool pack_counts(const Dims& d) {
@@ -383,19 +407,26 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     HandleRecord* meta = reinterpret_cast<HandleRecord*>(direct ? ws.recv_meta : ws.send_meta);
     if (pack_counts(d)) {
         const int mi = staging_ids_per_thread(d.Na, B);
+        const int tpb = tokens_per_block(d);
         auto pick = [&](auto fp8, auto dir) {
             constexpr bool F = decltype(fp8)::value, D = decltype(dir)::value;
-            return mi == 4 ? count_pack_kernel<F, D, 4> : mi == 8 ? count_pack_kernel<F, D, 8> : count_pack_kernel<F, D, 16>;
+            if (tpb == 4) return mi == 4 ? count_pack_kernel<F, D, 4, 4> : mi == 8 ? count_pack_kernel<F, D, 8, 4>
+                                                                                   : count_pack_kernel<F, D, 16, 4>;
+            if (tpb == 2) return mi == 4 ? count_pack_kernel<F, D, 4, 2> : mi == 8 ? count_pack_kernel<F, D, 8, 2>
+                                                                                   : count_pack_kernel<F, D, 16, 2>;
+            return mi == 4 ? count_pack_kernel<F, D, 4, 1> : mi == 8 ? count_pack_kernel<F, D, 8, 1>
+                                                                     : count_pack_kernel<F, D, 16, 1>;
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
         const size_t lds = 4 * std::max<size_t>(3 * (size_t)d.E, (size_t)mi * B);   // histograms | staged ids
-        launch_kernel(kernel, dim3((unsigned)(d.P + d.T), (unsigned)slices), dim3(B), lds, st,
-                           reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
-                           ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
-                           ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
-                           L);
+        const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
+        launch_kernel(kernel, dim3(blocks, (unsigned)slices), dim3(B), lds, st,
+                      reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
+                      ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
+                      ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
+                      L);
         return hipGetLastError();
     }
     const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));

@@ -163,6 +163,8 @@ EDGE = [
     ("count-chunks-Tp3000", 2, 3000, 256, 8, 64, False),
     ("E1024-top32", 4, 40, 1024, 32, 128, True),
     ("E1024-top32-wide-rows", 4, 4, 1024, 32, 7168, False),
+    ("two-tokens-per-block-ragged", 5, 205, 10, 3, 4096, False),
+    ("four-tokens-per-block-ragged", 2, 1025, 8, 2, 4352, True),
     ("E-odd-96", 3, 50, 96, 5, 520, False),
 ]
 
