@@ -230,10 +230,14 @@ const char* moe_status_string(moe_status status);
 const char* moe_last_error(void);
 
 /* Per-kernel timing: between moe_timing_begin and moe_timing_end every kernel
- * the ctx launches is bracketed by two HIP events on its stream.
- * moe_timing_end waits for the recorded events, writes up to `max` records
- * (one per kernel name, in first-launch order) and returns how many kernels
- * were seen in *count.  Timing adds two event records per launch. */
+ * the ctx launches carries a start and a stop HIP event in its own dispatch
+ * (hipExtLaunchKernelGGL), so a duration covers that kernel's execution and
+ * not the gaps between launches.  moe_timing_end waits for the recorded
+ * events, writes up to `max` records (one per kernel name, in first-launch
+ * order) and returns how many kernels were seen in *count.  Kernel names:
+ * route_topk, count, scan, pack, count_pack (the pack kernel counting by
+ * itself, small problems), exchange, stub, reverse_exchange, reduce, and
+ * pack_direct, count_pack_direct, reduce_direct for the direct forms. */
 moe_status moe_timing_begin(moe_ctx* ctx);
 moe_status moe_timing_end(moe_ctx* ctx, moe_kernel_time* out, int32_t max, int32_t* count);
 
