@@ -197,16 +197,18 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
 
 // Counts and offsets of source rank s for the handle (one workgroup of the
 // counting form per rank): LDS histograms of all ids, of the ids of ranks
-// below s and of rank s's ids, then exclusive scans over the experts.
+// below s and of rank s's ids, then one exclusive scan over the experts of
+// both the all-ranks and the rank-s counts (16 bits each: N_a <= 8192).
 __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int E, int Ep, int k, int P, int Na,
                             int32_t* __restrict__ n, int32_t* __restrict__ N, int32_t* __restrict__ C,
                             int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_recv_off,
                             int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off) {
-    extern __shared__ __align__(16) int32_t hist[];   // [3][E]: all ranks, ranks < s, rank s
+    extern __shared__ __align__(16) int32_t hist[];   // [4][E]: all ranks, ranks < s, rank s, rank s's scan
     __shared__ int32_t tmp[17];
     int32_t* h_all = hist;
     int32_t* h_lo = hist + E;
     int32_t* h_s = hist + 2 * E;
+    int32_t* x_s = hist + 3 * E;
     const int tid = threadIdx.x, bs = blockDim.x;
     const int lo = s * Tp * k, hi = lo + Tp * k;   // rank s's assignments
     int id[kMaxIdsPerThread];                    // all loads in flight at once (Na <= kMaxIdsPerThread * bs)
@@ -227,44 +229,49 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
         else if (a < hi) atomicAdd(&h_s[e], 1);
     }
     lds_barrier();
-    for (int r = tid; r < P; r += bs) {
-        int c = 0;
-        for (int e = r * Ep; e < (r + 1) * Ep; ++e) c += h_s[e];
-        C[(size_t)s * P + r] = c;
-    }
-    int carry_all = 0, carry_s = 0;
-    for (int e0 = 0; e0 < E; e0 += bs) {          // uniform loop: every thread calls the scans
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += bs) {          // uniform loop: every thread calls the scan
         const int e = e0 + tid;
-        const int ca = e < E ? h_all[e] : 0;
         const int cs = e < E ? h_s[e] : 0;
-        int tot_a, tot_s;
-        const int xa = block_exclusive_scan(ca, tmp, &tot_a);
-        const int xs = block_exclusive_scan(cs, tmp, &tot_s);
+        const int v = e < E ? h_all[e] + (cs << 16) : 0;
+        int tot;
+        const int x = carry + block_exclusive_scan(v, tmp, &tot);
         if (e < E) {
-            const int eo = carry_all + xa;
+            const int eo = x & 0xFFFF, xs = x >> 16;
+            x_s[e] = xs;
             n[(size_t)s * E + e] = cs;
-            send_off[(size_t)s * E + e] = lo + carry_s + xs;
+            send_off[(size_t)s * E + e] = lo + xs;
             recv_off[(size_t)s * E + e] = eo + h_lo[e];
             if (s == 0) {
-                N[e] = ca;
+                N[e] = h_all[e];
                 expert_off[e] = eo;
                 if (e % Ep == 0) rank_recv_off[e / Ep] = eo;
             }
         }
-        carry_all += tot_a;
-        carry_s += tot_s;
+        carry += tot;
     }
+    lds_barrier();
+    // C[s][r]: rank s's assignments to rank r's experts, from the scan
+    for (int r = tid; r < P; r += bs)
+        C[(size_t)s * P + r] = (r + 1 < P ? x_s[(r + 1) * Ep] : (carry >> 16)) - x_s[r * Ep];
     if (s == 0 && tid == 0) {
-        expert_off[E] = carry_all;
-        rank_recv_off[P] = carry_all;
+        expert_off[E] = carry & 0xFFFF;
+        rank_recv_off[P] = carry & 0xFFFF;
     }
 }
 
 // Grid (P + ceil(T / TPB), slices): block s < P of slice 0 writes rank s's
 // counts and offsets (the other slices of those blocks exit); block P + b packs
-// tokens b*TPB .. b*TPB + TPB - 1, whose TPB * k <= 32 assignments ("slots")
-// share one staging and counting pass.  The counting blocks come first so they
-// run alongside the packing ones.
+// tokens b*TPB .. b*TPB + TPB - 1 (all on one rank: TPB divides T/P), whose
+// TPB * k <= 32 assignments ("slots") share one counting pass.  The counting
+// blocks come first so they run alongside the packing ones.
+//
+// For slot (t, j) with expert e on rank s, and t0 the block's first token:
+//   recv_pos = #{a : id_a < e} + #{a < t0*k : id_a = e} + c
+//   send_pos = s*(T/P)*k + #{a on rank s : id_a < e} + #{a on rank s, a < t0*k : id_a = e} + c
+// with c = #{t0*k <= a < t*k : id_a = e} (earlier tokens of the same block).
+// Four LDS histograms of the ids (all, before t0, rank s, rank s before t0)
+// and one prefix sum give the first two terms of both.
 template <bool FP8, bool DIRECT, int MI, int TPB>
 __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
                                                          const float* __restrict__ w, uint4* __restrict__ dst,
@@ -279,7 +286,8 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
                                                          int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off,
                                                          int T, int Tp, int E, int Ep, int k, int P, int L) {
     __shared__ int32_t pos[32];
-    __shared__ int32_t red[32][8];             // per-slot wave partial counts; <= 8 waves
+    __shared__ int32_t blk[32];                // the block's own expert ids
+    __shared__ int32_t tmp[17];
     const int slice = blockIdx.y;
     const int tid = threadIdx.x, bs = blockDim.x;
     const int Na = T * k;
@@ -291,68 +299,71 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     const int t0 = ((int)blockIdx.x - P) * TPB;
     const int ntok = min(TPB, T - t0);
     const int nslots = ntok * k;               // <= 32 by the launch condition
+    const int s = t0 / Tp;                     // the block's rank
     const int u = slice * bs + tid;
+    const int t0k = t0 * k, lo = s * Tp * k, hi = lo + Tp * k;
 
     // the ids first (coalesced, all in flight at once), then the tokens' rows: the
     // counting below waits for the ids only, and LDS-only barriers keep the rows'
     // loads in flight until the rows are stored
     // (MI ids per thread, MI * blockDim.x >= N_a; straight-line code with clamped
     // addresses, so the waits for the ids do not also wait for the rows)
-    extern __shared__ __align__(16) int32_t staged[];   // [MI * blockDim.x], ids beyond N_a unused
     int raw[MI];
 #pragma unroll
     for (int m = 0; m < MI; ++m) raw[m] = ids[min(tid + m * bs, Na - 1)];
-    const float wt = w[t0 * k + min(tid, nslots - 1)];   // used by threads < nslots
+    const int sl = min(tid, nslots - 1);       // threads < nslots own a slot
+    const int my_e = ids[t0k + sl];
+    const float wt = w[t0k + sl];
     __builtin_amdgcn_sched_barrier(0);
     uint4 xa[TPB], xb[TPB];
 #pragma unroll
     for (int i = 0; i < TPB; ++i) load_row<FP8, false>(x, min(t0 + i, T - 1), L, u, xa[i], xb[i]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < MI; ++m) staged[tid + m * bs] = raw[m];
-    lds_barrier();
 
-    // lane (sl, sub) of a wave counts, for slot sl = lane mod kp (token t0 + sl / k,
-    // top-k slot sl % k), the ids of its run of the wave's share: receive count in
-    // the low half, same-rank count in the high half of one word (each is below
-    // N_a <= 8192); an xor butterfly over the g lanes of a slot then sums the
-    // wave's runs
-    const int lane = tid & (kWave - 1), wave = tid / kWave, nw = bs / kWave;
-    int kp = 1;
-    while (kp < nslots) kp <<= 1;              // nslots <= 32, so g >= 2 lanes per slot
-    const int g = kWave / kp;
-    const int sl = lane & (kp - 1), sub = lane / kp;
-    const int per_wave = (Na + nw - 1) / nw;
-    const int chunk = (per_wave + 4 * g - 1) / (4 * g) * (4 * g);
-    const int run = chunk / g;                 // a multiple of 4: 16-byte LDS reads stay aligned
-    const int base = wave * chunk + sub * run;
-    const int my_slot = min(sl, nslots - 1);
-    const int tk = t0 * k + my_slot - my_slot % k;   // first assignment of this slot's token
-    const int lo = (tk / k) / Tp * Tp * k, hi = lo + Tp * k;   // its rank's assignments
-    const int thr = sl < nslots ? (int)(2u * (unsigned)staged[t0 * k + sl] + 1u) : (int)0x80000000;   // padding counts nothing
-    int c = 0;
-    for (int i = 0; i < run; i += 4) {
-        const int a0 = base + i;
-        if (a0 >= Na) break;
-        const int4 v = *reinterpret_cast<const int4*>(&staged[a0]);
-        const int vv[4] = {v.x, v.y, v.z, v.w};
+    extern __shared__ __align__(16) int32_t hist[];   // [5][E]: all, before t0, rank s, rank s before t0, prefix
+    int32_t* h_all = hist;
+    int32_t* h_before = hist + E;
+    int32_t* h_rank = hist + 2 * E;
+    int32_t* h_rank_before = hist + 3 * E;
+    int32_t* prefix = hist + 4 * E;            // exclusive prefix of h_all (low 16 bits) and h_rank (high 16 bits)
+    for (int x = tid; x < 4 * E; x += bs) hist[x] = 0;
+    if (tid < nslots) blk[tid] = my_e;
+    lds_barrier();
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int a = a0 + e4;
-            const int key = (int)(2u * (unsigned)vv[e4] + (a >= tk ? 1u : 0u));
-            if (a < Na && key < thr) c += (a >= lo && a < hi) ? 0x10001 : 1;
+    for (int m = 0; m < MI; ++m) {
+        const int a = tid + m * bs;
+        const int e = raw[m];
+        if (a < Na && (unsigned)e < (unsigned)E) {   // out-of-range ids are outside the contract: never indexed
+            atomicAdd(&h_all[e], 1);
+            if (a < t0k) atomicAdd(&h_before[e], 1);
+            if (a >= lo && a < hi) {
+                atomicAdd(&h_rank[e], 1);
+                if (a < t0k) atomicAdd(&h_rank_before[e], 1);
+            }
         }
     }
-    for (int mask = kp; mask < kWave; mask <<= 1) c += __shfl_xor(c, mask);
-    if (sub == 0 && sl < nslots) red[sl][wave] = c;
+    lds_barrier();
+    // both prefix sums in one scan (each count is below N_a <= 8192, so 16 bits each)
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += bs) {       // uniform loop: every thread calls the scan
+        const int e = e0 + tid;
+        const int v = e < E ? h_all[e] + (h_rank[e] << 16) : 0;
+        int tot;
+        const int ex = block_exclusive_scan(v, tmp, &tot);
+        if (e < E) prefix[e] = carry + ex;
+        carry += tot;
+    }
     lds_barrier();
     int p = 0, q = 0;
     if (tid < nslots) {
-        int c = 0;
-        for (int v = 0; v < nw; ++v) c += red[tid][v];
-        const int t = t0 + tid / k;
-        q = c & 0xFFFF;
-        p = t / Tp * Tp * k + (c >> 16);
+        const int e = min(max(my_e, 0), E - 1);   // in range for any input (out-of-range ids are outside the contract)
+        int c = 0;                              // earlier tokens of this block with the same expert
+        for (int b = 0; b < tid - tid % k; ++b) c += blk[b] == my_e ? 1 : 0;
+        const int pe = prefix[e];
+        q = (pe & 0xFFFF) + h_before[e] + c;
+        p = lo + (pe >> 16) + h_rank_before[e] + c;
+        q = min(q, Na - 1);                     // no-ops for valid input; keep every write in bounds
+        p = min(p, hi - 1);
         pos[tid] = DIRECT ? q : p;
     }
     lds_barrier();
@@ -361,8 +372,8 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
         if (i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
     if (tid < nslots && slice == 0) {
         const int t = t0 + tid / k;
-        write_handle<DIRECT>(t0 * k + tid, t, t / Tp, Tp, tid % k, staged[t0 * k + tid], Ep, p, q, wt, dst_meta,
-                             send_to_recv, recv_to_send, send_pos, recv_pos);
+        write_handle<DIRECT>(t0k + tid, t, s, Tp, tid % k, my_e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send,
+                             send_pos, recv_pos);
     }
 }
 
@@ -382,7 +393,7 @@ int tokens_per_block(const Dims& d) {
     const int B = pick_block(d.row_units);
     const long long slices = (d.row_units + B - 1) / B;
     for (int tpb = 4; tpb > 1; tpb /= 2)
-        if (tpb * d.k <= 32 && (long long)(d.T / tpb) * slices >= 1024) return tpb;
+        if (tpb * d.k <= 32 && d.Tp % tpb == 0 && (long long)(d.T / tpb) * slices >= 1024) return tpb;
     return 1;
 }
 
@@ -420,7 +431,7 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         using T_ = std::true_type;
         using F_ = std::false_type;
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
-        const size_t lds = 4 * std::max<size_t>(3 * (size_t)d.E, (size_t)mi * B);   // histograms | staged ids
+        const size_t lds = 4 * 5 * (size_t)d.E;   // the counting blocks use 3 E, the packing blocks 5 E ints
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
         launch_kernel(kernel, dim3(blocks, (unsigned)slices), dim3(B), lds, st,
                       reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,

@@ -163,14 +163,15 @@ EDGE = [
     ("count-chunks-Tp3000", 2, 3000, 256, 8, 64, False),
     ("E1024-top32", 4, 40, 1024, 32, 128, True),
     ("E1024-top32-wide-rows", 4, 4, 1024, 32, 7168, False),
-    ("two-tokens-per-block-ragged", 5, 205, 10, 3, 4096, False),
-    ("four-tokens-per-block-ragged", 2, 1025, 8, 2, 4352, True),
+    ("two-tokens-per-block", 6, 342, 12, 3, 4096, False),
+    ("four-tokens-per-block-fp8", 4, 1024, 8, 2, 8192, True),
     ("E-odd-96", 3, 50, 96, 5, 520, False),
 ]
 
 
 @pytest.mark.parametrize("policy,count,direct", [("auto", "auto", False), ("streaming", "auto", False),
-                                                 ("auto", "auto", True), ("auto", "separate", False)])
+                                                 ("auto", "auto", True), ("auto", "separate", False),
+                                                 ("auto", "fused", True)])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, count, direct):
     monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
