@@ -333,6 +333,29 @@ def main():
         cold_ms = float(np.median(times))
         del flush
 
+    # the step captured once in a HIP graph and replayed (no per-call host work)
+    def graph_ms(direct):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            B.run_path(ctx, bufs, x, logits, None, direct=direct)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            B.run_path(ctx, bufs, x, logits, None, direct=direct)
+        for _ in range(args.warmup):
+            g.replay()
+        ms = timed(g.replay, args.steps)
+        del g
+        return ms
+
+    graph = {}
+    for mode, d in (("base", False), ("direct", True)):
+        ms = graph_ms(d)
+        graph[mode] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
+    step()   # leave the buffers as the measured form wrote them
+
     kb = kernel_bytes(w)
     per_kernel = {}
     phases = {}
@@ -380,6 +403,7 @@ def main():
             "dispatch_combine_tokens_per_s": round(T / (other_dc_ms * 1e-3), 1),
             "dispatch_combine_gbps": round(other_dc_bytes / (other_dc_ms * 1e-3) / 1e9, 1),
         },
+        "graph_replay": graph,
         "phases_ms": {k: round(v, 5) for k, v in phases.items()},
         "kernels": per_kernel,
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),

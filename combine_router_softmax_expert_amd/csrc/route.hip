@@ -19,8 +19,9 @@
 // Softmax is strictly increasing, so selecting by logit is selecting by
 // probability, and the renormalised weight p_j / sum_sel p equals
 // exp(l_j - l_max) / sum_sel exp(l_i - l_max): the full partition function
-// cancels.  Those k exponentials and the slot-order sum run in double, so the
-// fp32 weights are the correctly rounded ones up to a double ulp.
+// cancels.  Those k exponentials (evaluated together, one per lane, after the
+// selection) and the slot-order sum run in double, so the fp32 weights are the
+// correctly rounded ones up to a double ulp.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         if (valid && e < E) key[v] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)~(uint32_t)e;
     }
 
-    double m = 0.0, sum = 0.0, my_e = 0.0;
+    double my_l = 0.0;
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
         uint64_t best = key[0];
@@ -72,11 +73,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 #pragma unroll
         for (int v = 0; v < V; ++v)
             if (gl + G * v == id) key[v] = 0;
-        if (j == 0) m = lv;
-        const double ej = exp(lv - m);
-        sum += ej;                       // slot order
-        if (gl == j) { my_id = id; my_e = ej; }
+        if (gl == j) { my_id = id; my_l = lv; }
     }
+    // the k exponentials at once (lanes gl < k), then their sum in slot order
+    const double m = __shfl(my_l, 0, G);
+    const double my_e = gl < k ? exp(my_l - m) : 0.0;
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += __shfl(my_e, j, G);
     if (valid && gl < k) {
         ids[(size_t)t * k + gl] = my_id;
         w[(size_t)t * k + gl] = (float)(my_e / sum);
@@ -99,6 +102,14 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
+// Lane l's double, in every lane.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)b, l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 template <int V>
 __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __restrict__ logits,
                                                               int32_t* __restrict__ ids, float* __restrict__ w,
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
         const int e = lane + kWave * v;
         val[v] = e < E ? row[e] : nan;
     }
-    double m = 0.0, sum = 0.0, my_e = 0.0;
+    float my_l = 0.0f;
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
         float lm = val[0];
@@ -130,12 +141,13 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
 #pragma unroll
         for (int v = 0; v < V; ++v)
             if (lane + kWave * v == id) val[v] = nan;
-        const double lv = (double)M;
-        if (j == 0) m = lv;
-        const double ej = exp(lv - m);
-        sum += ej;                       // slot order
-        if (lane == j) { my_id = id; my_e = ej; }
+        if (lane == j) { my_id = id; my_l = M; }
     }
+    // the k exponentials at once (lanes < k), then their sum in slot order
+    const double l0 = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+    const double my_e = lane < k ? exp((double)my_l - l0) : 0.0;
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += readlane_f64(my_e, j);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
         w[(size_t)t * k + lane] = (float)(my_e / sum);
