@@ -33,9 +33,10 @@ struct moe_ctx {
     moe::Dims d;
     // byte offsets of the workspace arrays
     size_t o_n, o_N, o_expert_off, o_rank_recv_off, o_send_off, o_recv_off, o_C, o_bucket_rank, o_send_pos,
-        o_recv_pos, o_send_to_recv, o_recv_to_send, o_send_meta, o_recv_meta, ws_bytes;
+        o_recv_pos, o_send_to_recv, o_recv_to_send, o_send_meta, o_recv_meta, o_bad_ids, ws_bytes;
     uint64_t generation = 0;
     bool timing = false;
+    bool debug = false;    // MOE_EP_DEBUG: validate ids on the device (and synchronise) before dispatching
     std::vector<TimingRecord> records;
     std::vector<hipEvent_t> free_events;
 };
@@ -94,6 +95,7 @@ moe::Workspace carve(const moe_ctx* ctx, void* base) {
     w.recv_to_send = reinterpret_cast<int32_t*>(p + ctx->o_recv_to_send);
     w.send_meta = p + ctx->o_send_meta;
     w.recv_meta = p + ctx->o_recv_meta;
+    w.bad_ids = reinterpret_cast<int32_t*>(p + ctx->o_bad_ids);
     return w;
 }
 
@@ -124,6 +126,24 @@ void fill_handle(moe_ctx* ctx, const moe::Workspace& ws, moe_handle* handle, boo
     handle->recv_meta = static_cast<const moe_meta*>(ws.recv_meta);
     handle->ctx = ctx;
     handle->generation = ctx->generation;
+}
+
+// Debug mode: count invalid ids on the device, wait for the answer and refuse
+// the dispatch if there are any (before any payload kernel is launched).
+moe_status validate_ids(moe_ctx* ctx, const moe::Dims& d, const int32_t* topk_ids, const moe::Workspace& ws,
+                        hipStream_t st) {
+    if (!ctx->debug) return MOE_OK;
+    hipError_t e = moe::launch_validate_ids(d, topk_ids, ws.bad_ids, st);
+    if (e != hipSuccess) return hip_fail(e, "validate_ids");
+    int32_t bad = 0;
+    e = hipMemcpyAsync(&bad, ws.bad_ids, sizeof(bad), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "validate_ids");
+    if (bad != 0) {
+        g_last_error = "topk_ids: " + std::to_string(bad) + " assignment(s) out of range or repeated within a token";
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
 }
 
 // The count kernel (and the scan kernel unless one workgroup does both).
@@ -198,6 +218,8 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
         if (std::strcmp(pol, "temporal") == 0) d.policy = moe::CachePolicy::kTemporal;
         if (std::strcmp(pol, "streaming") == 0) d.policy = moe::CachePolicy::kStreaming;
     }
+    // MOE_EP_DEBUG=1: dispatch checks the ids on the device first (see validate_ids)
+    if (const char* dbg = std::getenv("MOE_EP_DEBUG")) ctx->debug = std::strcmp(dbg, "0") != 0 && dbg[0] != 0;
     // MOE_EP_COUNT_PATH=separate|fused overrides the size-based choice (for A/B tests)
     d.count_path = moe::CountPath::kAuto;
     if (const char* cp = std::getenv("MOE_EP_COUNT_PATH")) {
@@ -222,6 +244,7 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
     ctx->o_recv_to_send = take(4 * tk);
     ctx->o_send_meta = take(sizeof(moe_meta) * tk);
     ctx->o_recv_meta = take(sizeof(moe_meta) * tk);
+    ctx->o_bad_ids = take(4);
     ctx->ws_bytes = off;
     *out = ctx;
     return MOE_OK;
@@ -266,6 +289,8 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
     hipStream_t st = static_cast<hipStream_t>(stream);
     moe_status s = MOE_OK;
     if (d.T > 0) {
+        s = validate_ids(ctx, d, topk_ids, ws, st);
+        if (s != MOE_OK) return s;
         const bool fused = moe::pack_counts(d);
         if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
         if (s == MOE_OK)
@@ -295,8 +320,10 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (d.T > 0) {
+        moe_status s = validate_ids(ctx, d, topk_ids, ws, st);
+        if (s != MOE_OK) return s;
         const bool fused = moe::pack_counts(d);
-        moe_status s = fused ? MOE_OK : count_and_scan(ctx, d, topk_ids, ws, st);
+        if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
         if (s == MOE_OK)
             s = launch(ctx, fused ? "count_pack_direct" : "pack_direct", st, [&] {
                 return moe::launch_pack(d, x, topk_ids, topk_w, ws, recv_buf, recv_scales, true, st);

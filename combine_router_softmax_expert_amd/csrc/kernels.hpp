@@ -69,8 +69,11 @@ struct Workspace {         // device arrays carved from the caller's workspace
     int32_t* recv_to_send; // [N_a] send row of each receive row
     void* send_meta;       // [N_a] 16-byte records
     void* recv_meta;       // [N_a]
+    int32_t* bad_ids;      // [1] debug mode: number of invalid assignments found
 };
 
+// Debug check: the number of ids outside [0, E) or repeated within a token.
+hipError_t launch_validate_ids(const Dims& d, const int32_t* ids, int32_t* bad_out, hipStream_t st);
 hipError_t launch_route_topk(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st);

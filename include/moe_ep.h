@@ -30,6 +30,10 @@
  *  - Host-detectable errors are returned synchronously and nothing is
  *    enqueued; launch failures return MOE_ERR_HIP.  Expert ids outside
  *    [0, E) or repeated within a token are outside the contract.
+ *  - Debug mode (environment MOE_EP_DEBUG=1 when the ctx is created): both
+ *    dispatch calls first count such ids on the device, wait for the count
+ *    (the one place the library synchronises) and return MOE_ERR_INVALID_ARG,
+ *    with the count in moe_last_error(), before launching anything else.
  *  - T = 0 is a valid no-op.  No C++ exception crosses this ABI.
  */
 #ifndef MOE_EP_H
