@@ -68,6 +68,10 @@ def _load():
         "moe_combine": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
         "moe_dispatch_direct": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_combine_direct": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
+        "moe_dispatch_send": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
+        "moe_dispatch_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
+        "moe_combine_send": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P]),
+        "moe_combine_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_begin": (I32, [P]),
@@ -260,6 +264,51 @@ def moe_combine_direct(ctx: Context, handle: MoeHandle, expert_out, topk_w, y, s
            "moe_combine_direct")
 
 
+def moe_dispatch_send(ctx: Context, x, topk_ids, topk_w, workspace, send_buf, send_scales, stream=None) -> MoeHandle:
+    import torch
+    T, H, k, Na = ctx.T, ctx.H, ctx.k, ctx.num_assignments
+    rb, nb = ctx.row_bytes, ctx.scales_per_row
+    h = MoeHandle()
+    ws = _ptr(workspace, None, ctx.workspace_bytes, "workspace")
+    _check(lib.moe_dispatch_send(ctx.handle_ptr, _ptr(x, (torch.bfloat16, torch.int16), 2 * T * H, "x"),
+                                 _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                                 _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                 ws, workspace.numel() * workspace.element_size(),
+                                 _ptr(send_buf, None, Na * rb, "send_buf"),
+                                 _ptr(send_scales, torch.float32, 4 * Na * nb, "send_scales"),
+                                 ctypes.byref(h), _stream(stream)), "moe_dispatch_send")
+    return h
+
+
+def moe_dispatch_recv(ctx: Context, handle: MoeHandle, send_buf, send_scales, recv_buf, recv_scales, stream=None):
+    import torch
+    Na, rb, nb = ctx.num_assignments, ctx.row_bytes, ctx.scales_per_row
+    _check(lib.moe_dispatch_recv(ctx.handle_ptr, ctypes.byref(handle), _ptr(send_buf, None, Na * rb, "send_buf"),
+                                 _ptr(send_scales, torch.float32, 4 * Na * nb, "send_scales"),
+                                 _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                                 _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"), _stream(stream)),
+           "moe_dispatch_recv")
+
+
+def moe_combine_send(ctx: Context, handle: MoeHandle, expert_out, comb_buf, stream=None):
+    import torch
+    Na, H = ctx.num_assignments, ctx.H
+    _check(lib.moe_combine_send(ctx.handle_ptr, ctypes.byref(handle),
+                                _ptr(expert_out, (torch.bfloat16, torch.int16), 2 * Na * H, "expert_out"),
+                                _ptr(comb_buf, (torch.bfloat16, torch.int16), 2 * Na * H, "comb_buf"),
+                                _stream(stream)), "moe_combine_send")
+
+
+def moe_combine_recv(ctx: Context, handle: MoeHandle, comb_buf, topk_w, y, stream=None):
+    import torch
+    Na, H, T, k = ctx.num_assignments, ctx.H, ctx.T, ctx.k
+    _check(lib.moe_combine_recv(ctx.handle_ptr, ctypes.byref(handle),
+                                _ptr(comb_buf, (torch.bfloat16, torch.int16), 2 * Na * H, "comb_buf"),
+                                _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
+           "moe_combine_recv")
+
+
 def moe_timing_begin(ctx: Context):
     _check(lib.moe_timing_begin(ctx.handle_ptr), "moe_timing_begin")
 
@@ -286,3 +335,37 @@ def run_path(ctx: Context, bufs: dict, x, logits, stream=None, direct: bool = Fa
     else:
         moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
     return h
+
+
+def run_overlapped(parts, comm_stream, compute_stream):
+    """Micro-batches through the split phases on two streams.
+
+    ``parts`` is a list of (ctx, bufs, x, logits), one independent problem per
+    micro-batch.  Routing, both dispatch halves and both combine halves run on
+    ``comm_stream``, the expert stage on ``compute_stream``; events order each
+    micro-batch's stages, so the expert stage of micro-batch i can overlap the
+    dispatch of i+1 and the combine of i-1 ([PPLX]: send and receive halves let
+    other work run in between).  Only launches and events: the caller
+    synchronises before reading the outputs.  Returns the handles."""
+    import torch
+    handles, dispatched, computed = [], [], []
+    for ctx, bufs, x, logits in parts:
+        moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"], comm_stream)
+        h = moe_dispatch_send(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                              bufs["send_scales"], comm_stream)
+        moe_dispatch_recv(ctx, h, bufs["send"], bufs["send_scales"], bufs["recv"], bufs["recv_scales"], comm_stream)
+        ev = torch.cuda.Event()
+        ev.record(comm_stream)
+        handles.append(h)
+        dispatched.append(ev)
+    for (ctx, bufs, _, _), h, ev in zip(parts, handles, dispatched):
+        compute_stream.wait_event(ev)
+        moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"], compute_stream)
+        done = torch.cuda.Event()
+        done.record(compute_stream)
+        computed.append(done)
+    for (ctx, bufs, _, _), h, ev in zip(parts, handles, computed):
+        comm_stream.wait_event(ev)
+        moe_combine_send(ctx, h, bufs["expert_out"], bufs["comb"], comm_stream)
+        moe_combine_recv(ctx, h, bufs["comb"], bufs["topk_w"], bufs["y"], comm_stream)
+    return handles

@@ -35,6 +35,9 @@ struct moe_ctx {
     size_t o_n, o_N, o_expert_off, o_rank_recv_off, o_send_off, o_recv_off, o_C, o_bucket_rank, o_send_pos,
         o_recv_pos, o_send_to_recv, o_recv_to_send, o_send_meta, o_recv_meta, o_bad_ids, ws_bytes;
     uint64_t generation = 0;
+    uint64_t received = 0;       // generation whose receive side is complete (exchange or direct pack)
+    uint64_t combine_sent = 0;   // generation whose reverse exchange was issued
+    void* workspace = nullptr;   // workspace of the latest dispatch (the split receive phase reads its maps)
     bool timing = false;
     bool debug = false;    // MOE_EP_DEBUG: validate ids on the device (and synchronise) before dispatching
     std::vector<TimingRecord> records;
@@ -161,6 +164,17 @@ moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
     return MOE_OK;
 }
 
+// The stages after the exchange need the receive side of the handle's dispatch.
+moe_status check_received(const moe_ctx* ctx, const moe_handle* h, const char* who) {
+    moe_status s = check_handle(ctx, h);
+    if (s != MOE_OK) return s;
+    if (ctx->received != h->generation) {
+        g_last_error = std::string(who) + ": moe_dispatch_recv has not been issued for this handle";
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,22 +288,20 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, 
     return launch(ctx, "route_topk", st, [&] { return moe::launch_route_topk(d, logits, topk_ids, topk_w, st); });
 }
 
-moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
-                        void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
-                        void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                             void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
+                             moe_handle* handle, void* stream) {
     if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
     const moe::Dims d = ctx->d;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
-    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf || !recv_buf)) return MOE_ERR_INVALID_ARG;
-    if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
-        return MOE_ERR_INVALID_ARG;
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return MOE_ERR_INVALID_ARG;
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    moe_status s = MOE_OK;
     if (d.T > 0) {
-        s = validate_ids(ctx, d, topk_ids, ws, st);
+        moe_status s = validate_ids(ctx, d, topk_ids, ws, st);
         if (s != MOE_OK) return s;
         const bool fused = moe::pack_counts(d);
         if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
@@ -297,14 +309,50 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
             s = launch(ctx, fused ? "count_pack" : "pack", st, [&] {
                 return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, false, st);
             });
-        if (s == MOE_OK)
-            s = launch(ctx, "exchange", st, [&] {
-                return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, st);
-            });
         if (s != MOE_OK) return s;
     }
+    ctx->workspace = workspace;
     fill_handle(ctx, ws, handle, true);
     return MOE_OK;
+}
+
+moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
+                             void* recv_buf, float* recv_scales, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_handle(ctx, handle);
+    if (s != MOE_OK) return s;
+    if (!handle->send_meta || ctx->received == ctx->generation) {
+        g_last_error = "moe_dispatch_recv: the handle's receive side is already complete";
+        return MOE_ERR_INVALID_ARG;
+    }
+    const moe::Dims d = ctx->d;
+    if (d.T > 0 && (!send_buf || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
+        return MOE_ERR_INVALID_ARG;
+    if (d.T > 0) {
+        const moe::Workspace ws = carve(ctx, ctx->workspace);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        s = launch(ctx, "exchange", st, [&] {
+            return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, st);
+        });
+        if (s != MOE_OK) return s;
+    }
+    ctx->received = ctx->generation;
+    return MOE_OK;
+}
+
+moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                        void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
+                        void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const moe::Dims d = ctx->d;
+    // every argument is checked before anything is enqueued
+    if (d.T > 0 && !recv_buf) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    moe_status s = moe_dispatch_send(ctx, x, topk_ids, topk_w, workspace, workspace_bytes, send_buf, send_scales,
+                                     handle, stream);
+    if (s != MOE_OK) return s;
+    return moe_dispatch_recv(ctx, handle, send_buf, send_scales, recv_buf, recv_scales, stream);
 }
 
 moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
@@ -330,14 +378,16 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
             });
         if (s != MOE_OK) return s;
     }
+    ctx->workspace = workspace;
     fill_handle(ctx, ws, handle, false);
+    ctx->received = ctx->generation;
     return MOE_OK;
 }
 
 moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf, const float* recv_scales,
                            uint16_t* expert_out, void* stream) {
     if (!ctx) return MOE_ERR_INVALID_ARG;
-    moe_status s = check_handle(ctx, handle);
+    moe_status s = check_received(ctx, handle, "moe_expert_stub");
     if (s != MOE_OK) return s;
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
@@ -347,26 +397,55 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
     return launch(ctx, "stub", st, [&] { return moe::launch_stub(d, ws, recv_buf, recv_scales, expert_out, st); });
 }
 
+moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
+                            uint16_t* comb_buf, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_received(ctx, handle, "moe_combine_send");
+    if (s != MOE_OK) return s;
+    const moe::Dims d = ctx->d;
+    if (d.T > 0) {
+        if (!expert_out || !comb_buf) return MOE_ERR_INVALID_ARG;
+        const moe::Workspace ws = from_handle(handle);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        s = launch(ctx, "reverse_exchange", st,
+                   [&] { return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, st); });
+        if (s != MOE_OK) return s;
+    }
+    ctx->combine_sent = ctx->generation;
+    return MOE_OK;
+}
+
+moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
+                            uint16_t* y, void* stream) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_received(ctx, handle, "moe_combine_recv");
+    if (s != MOE_OK) return s;
+    if (ctx->combine_sent != handle->generation) {
+        g_last_error = "moe_combine_recv: moe_combine_send has not been issued for this handle";
+        return MOE_ERR_INVALID_ARG;
+    }
+    const moe::Dims d = ctx->d;
+    if (d.T == 0) return MOE_OK;
+    if (!comb_buf || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch(ctx, "reduce", st, [&] { return moe::launch_reduce(d, comb_buf, nullptr, topk_w, y, false, st); });
+}
+
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out, const float* topk_w,
                        uint16_t* comb_buf, uint16_t* y, void* stream) {
     if (!ctx) return MOE_ERR_INVALID_ARG;
-    moe_status s = check_handle(ctx, handle);
+    moe_status s = check_received(ctx, handle, "moe_combine");
     if (s != MOE_OK) return s;
-    const moe::Dims d = ctx->d;
-    if (d.T == 0) return MOE_OK;
-    if (!expert_out || !topk_w || !comb_buf || !y) return MOE_ERR_INVALID_ARG;
-    const moe::Workspace ws = from_handle(handle);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    s = launch(ctx, "reverse_exchange", st, [&] { return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, st); });
+    if (ctx->d.T > 0 && (!expert_out || !topk_w || !comb_buf || !y)) return MOE_ERR_INVALID_ARG;
+    s = moe_combine_send(ctx, handle, expert_out, comb_buf, stream);
     if (s != MOE_OK) return s;
-    return launch(ctx, "reduce", st,
-                  [&] { return moe::launch_reduce(d, comb_buf, nullptr, topk_w, y, false, st); });
+    return moe_combine_recv(ctx, handle, comb_buf, topk_w, y, stream);
 }
 
 moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                               const float* topk_w, uint16_t* y, void* stream) {
     if (!ctx) return MOE_ERR_INVALID_ARG;
-    moe_status s = check_handle(ctx, handle);
+    moe_status s = check_received(ctx, handle, "moe_combine_direct");
     if (s != MOE_OK) return s;
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;

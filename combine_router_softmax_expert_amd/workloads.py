@@ -193,3 +193,13 @@ def custom(name: str, P: int, T: int, E: int, k: int, H: int, dtype: str = BF16,
     if T % P:
         raise ValueError("T must be a multiple of P (tokens are blocked over ranks)")
     return Workload(name, P, T, E, k, H, dtype, seed, zipf)
+
+
+def micro_batch_rows(num_ranks: int, tokens_per_rank: int, parts: int, index: int) -> np.ndarray:
+    """Rows of the rank-blocked token matrix that form micro-batch ``index`` of
+    ``parts``: on every rank, its local tokens [index*Tp/parts, (index+1)*Tp/parts),
+    so each micro-batch is again rank-blocked with Tp/parts tokens per rank."""
+    assert tokens_per_rank % parts == 0 and 0 <= index < parts
+    n = tokens_per_rank // parts
+    local = np.arange(index * n, (index + 1) * n)
+    return (np.arange(num_ranks)[:, None] * tokens_per_rank + local[None, :]).reshape(-1)

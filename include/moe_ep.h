@@ -226,6 +226,33 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
 moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                               const float* topk_w, uint16_t* y, void* stream);
 
+/* ---- split phases ([PPLX]: dispatch and combine each run as a send half and
+ * a receive half, so that other work can run in between; [A2A] 7: overlap pays
+ * only when there is independent work to hide the exchange behind) --------- */
+
+/* moe_dispatch = moe_dispatch_send then moe_dispatch_recv; moe_combine =
+ * moe_combine_send then moe_combine_recv.  The halves may be issued on
+ * different streams; ordering them (an event recorded after one half and
+ * waited on before the next) is the caller's job.  The host enforces the call
+ * order per handle: the receive half of dispatch before the expert stage and
+ * the combine, the send half of combine before its receive half (else
+ * MOE_ERR_INVALID_ARG, reason in moe_last_error()).  Base form only.
+ *   moe_dispatch_send  count, prefix sums, pack into send_buf (+ scales) and the
+ *                      handle; arguments as moe_dispatch without the receive side
+ *   moe_dispatch_recv  the exchange into recv_buf (+ scales) and the receive records
+ *   moe_combine_send   the reverse exchange into comb_buf
+ *   moe_combine_recv   the weighted reduction of comb_buf into y
+ * Errors: as the corresponding whole calls. */
+moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                             void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
+                             moe_handle* handle, void* stream);
+moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
+                             void* recv_buf, float* recv_scales, void* stream);
+moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
+                            uint16_t* comb_buf, void* stream);
+moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
+                            uint16_t* y, void* stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 
 /* Static, human-readable text of a status code. */

@@ -168,3 +168,46 @@ def test_timing_without_launches(b):
     n = ctypes.c_int32(-1)
     assert b.lib.moe_timing_end(h, recs, 4, ctypes.byref(n)) == 0 and n.value == 0
     b.lib.moe_ctx_destroy(h)
+
+
+def test_split_phases_enforce_their_order(b):
+    """The host refuses a stage whose earlier half was not issued (T = 0: nothing is launched)."""
+    st, h = _create(b, Tp=0)
+    fake = ctypes.c_void_p(1 << 20)
+    ws = b.lib.moe_workspace_bytes(h)
+    hd = b.MoeHandle()
+    assert b.lib.moe_dispatch_send(h, None, None, None, fake, ws, None, None, ctypes.byref(hd), None) == 0
+    # the expert stage and the combine need the receive half first
+    assert b.lib.moe_expert_stub(h, ctypes.byref(hd), None, None, None, None) == -1
+    assert b"moe_dispatch_recv" in b.lib.moe_last_error()
+    assert b.lib.moe_combine(h, ctypes.byref(hd), None, None, None, None, None) == -1
+    assert b.lib.moe_dispatch_recv(h, ctypes.byref(hd), None, None, None, None, None) == 0
+    assert b.lib.moe_dispatch_recv(h, ctypes.byref(hd), None, None, None, None, None) == -1   # only once
+    assert b.lib.moe_expert_stub(h, ctypes.byref(hd), None, None, None, None) == 0
+    # the combine's receive half needs its send half
+    assert b.lib.moe_combine_recv(h, ctypes.byref(hd), None, None, None, None) == -1
+    assert b.lib.moe_combine_send(h, ctypes.byref(hd), None, None, None) == 0
+    assert b.lib.moe_combine_recv(h, ctypes.byref(hd), None, None, None, None) == 0
+    # a direct dispatch has no separate receive half
+    hdir = b.MoeHandle()
+    assert b.lib.moe_dispatch_direct(h, None, None, None, fake, ws, None, None, ctypes.byref(hdir), None) == 0
+    assert b.lib.moe_dispatch_recv(h, ctypes.byref(hdir), None, None, None, None, None) == -1
+    assert b.lib.moe_combine_direct(h, ctypes.byref(hdir), None, None, None, None) == 0
+    # a newer dispatch makes the older handle stale for every half
+    assert b.lib.moe_dispatch_recv(h, ctypes.byref(hd), None, None, None, None, None) == -4
+    b.lib.moe_ctx_destroy(h)
+
+
+def test_split_phases_validate_arguments(b):
+    st, h = _create(b)
+    fake = ctypes.c_void_p(1 << 20)
+    ws = b.lib.moe_workspace_bytes(h)
+    hd = b.MoeHandle()
+    S = b.lib.moe_dispatch_send
+    assert S(h, fake, fake, fake, fake, ws, None, None, ctypes.byref(hd), None) == -1      # no send buffer
+    assert S(h, fake, fake, fake, fake, ws, fake, fake, ctypes.byref(hd), None) == -1      # bf16 takes no scales
+    assert S(h, fake, fake, fake, fake, ws - 1, fake, None, ctypes.byref(hd), None) == -3
+    assert b.lib.moe_dispatch_recv(h, ctypes.byref(b.MoeHandle()), fake, None, fake, None, None) == -4
+    assert b.lib.moe_combine_send(h, ctypes.byref(b.MoeHandle()), fake, fake, None) == -4
+    assert b.lib.moe_combine_recv(h, ctypes.byref(b.MoeHandle()), fake, fake, fake, None) == -4
+    b.lib.moe_ctx_destroy(h)
