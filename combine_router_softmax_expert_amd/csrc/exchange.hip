@@ -29,7 +29,7 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
                                                        const float* __restrict__ send_scales,
                                                        float* __restrict__ recv_scales,
                                                        const uint4* __restrict__ send_meta,
-                                                       uint4* __restrict__ recv_meta, int L, int nb, int slices) {
+                                                       uint4* __restrict__ recv_meta, int L, int nb) {
     const int b = blockIdx.x;
     const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
 __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uint4* __restrict__ expert_out,
                                                                        uint4* __restrict__ comb,
                                                                        const HandleRecord* __restrict__ recv_meta, int Tp,
-                                                                       int k, int L, int slices) {
+                                                                       int k, int L) {
     const int q = blockIdx.x;
     const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;
@@ -69,8 +69,7 @@ __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uin
 
 __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint4* __restrict__ expert_out,
                                                                       uint4* __restrict__ comb,
-                                                                      const int32_t* __restrict__ recv_pos, int L,
-                                                                      int slices) {
+                                                                      const int32_t* __restrict__ recv_pos, int L) {
     const int c = blockIdx.x;                   // combine row t*k + j
     const int slice = blockIdx.y;
     const int q = recv_pos[c];
@@ -92,7 +91,7 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
                        reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
                        gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
                        reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L,
-                       d.scales, slices);
+                       d.scales);
     return hipGetLastError();
 }
 
@@ -104,12 +103,11 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int slices = (L + B - 1) / B;
     if (streaming(d, 2LL * d.Na * 16LL * L))
         launch_kernel(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
-                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
-                           slices);
+                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L);
     else
         launch_kernel(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
                            reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                           reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
+                           reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L);
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ constexpr long long kStreamingBytes = 128LL << 20;
 // How dispatch ranks the assignments: kAuto lets the pack kernel count by itself
 // when the problem is small enough (pack_counts), kSeparate always launches the
 // count (and scan) kernels first, kFused counts in the pack kernel whenever its
-// staging fits.
+// id loads fit (kMaxIdsPerThread per thread).
 enum class CountPath { kAuto = 0, kSeparate = 1, kFused = 2 };
 
 struct Dims {

@@ -25,7 +25,7 @@
 // scattered rows ran at 60% of the temporal bandwidth on gfx950).
 //
 // Counting form (small problems, where a separate count launch costs more than
-// the counting itself): every workgroup ranks its token's k assignments by
+// the counting itself): every workgroup ranks its tokens' k assignments by
 // itself from all N_a expert ids, which sit in the cache.  With tokens blocked
 // by rank and each token's experts distinct, the stable positions have a
 // closed form in counts (the send order is local expert then token, the
@@ -34,11 +34,10 @@
 // rank s,
 //   recv_pos = #{a : id_a < e} + #{a : id_a = e, token(a) < t}
 //   send_pos = s*(T/P)*k + the same two counts over rank s's assignments only.
-// Both are one compare per id against the key 2*id + [token(a) >= t] < 2e + 1:
-// the ids are staged in LDS, each lane counts a run of them for one of the k
-// slots, and xor shuffles and an LDS table sum the runs.  P extra workgroups, one per source rank,
-// write the counts and offsets of the handle (n, N, C, expert_off,
-// rank_recv_off, send_off, recv_off) from LDS histograms in the same launch.
+// LDS histograms of the ids and one prefix sum give these counts (see
+// count_pack_kernel).  P extra workgroups, one per source rank, write the
+// counts and offsets of the handle (n, N, C, expert_off, rank_recv_off,
+// send_off, recv_off) from LDS histograms in the same launch.
 #include <algorithm>
 #include <type_traits>
 
@@ -379,16 +378,17 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
 
 }  // namespace
 
-// Ids per thread of the counting form's staging loop: 4, 8 or 16.
-int staging_ids_per_thread(long long Na, int B) {
+// Ids each thread of the counting form loads (unrolled, all in flight): 4, 8 or 16.
+int ids_per_thread(long long Na, int B) {
     const long long m = (Na + B - 1) / B;
     return m <= 4 ? 4 : m <= 8 ? 8 : 16;
 }
 
-// Tokens per workgroup of the counting form: more tokens share one staging and
-// counting pass, as long as their slots fit one wave's lanes (TPB * k <= 32) and
-// at least 1024 workgroups remain (measured on gfx950 at 2048 tokens x top-2:
-// 2 tokens per workgroup 17.8 us, 1 token 20.7 us, 4 tokens 20.0 us).
+// Tokens per workgroup of the counting form: more tokens share one counting
+// pass, as long as their slots fit the per-workgroup tables (TPB * k <= 32), the
+// tokens of a workgroup share one rank (TPB divides T/P) and at least 1024
+// workgroups remain (measured on gfx950 at 2048 tokens x top-2: 2 tokens per
+// workgroup 13.4 us, 1 token 16.7 us, 4 tokens 13.6 us).
 int tokens_per_block(const Dims& d) {
     const int B = pick_block(d.row_units);
     const long long slices = (d.row_units + B - 1) / B;
@@ -401,10 +401,10 @@ bool pack_counts(const Dims& d) {
     if (d.T == 0 || d.count_path == CountPath::kSeparate) return false;
     const int B = pick_block(d.row_units);
     const long long blocks = (long long)d.T * ((d.row_units + B - 1) / B);
-    // every thread stages at most kMaxIdsPerThread ids, and the ids all workgroups
+    // every thread loads at most kMaxIdsPerThread ids, and the ids all workgroups
     // read together stay well below the payload (measured on gfx950: a win at
-    // 128 tokens x top-8 with 256 workgroups and at 2048 tokens x top-2 with 2048
-    // workgroups staging 4096 ids each)
+    // 128 tokens x top-8 with 256 workgroups and at 2048 tokens x top-2 with 1024
+    // workgroups reading 4096 ids each)
     if (d.Na > (long long)kMaxIdsPerThread * B) return false;
     return d.count_path == CountPath::kFused || blocks * d.Na <= (1LL << 24);
 }
@@ -417,7 +417,7 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     const int slices = (L + B - 1) / B;
     HandleRecord* meta = reinterpret_cast<HandleRecord*>(direct ? ws.recv_meta : ws.send_meta);
     if (pack_counts(d)) {
-        const int mi = staging_ids_per_thread(d.Na, B);
+        const int mi = ids_per_thread(d.Na, B);
         const int tpb = tokens_per_block(d);
         auto pick = [&](auto fp8, auto dir) {
             constexpr bool F = decltype(fp8)::value, D = decltype(dir)::value;

@@ -132,11 +132,11 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
 #pragma unroll
         for (int v = 1; v < V; ++v) lm = fmaxf(lm, val[v]);
         const float M = wave_max(lm);
-        int id = 0;
+        int id = -1;                     // the lowest expert id holding M
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const unsigned long long hit = __ballot(val[v] == M);
-            if (hit) { id = kWave * v + __ffsll((long long)hit) - 1; break; }
+            if (id < 0 && hit) id = kWave * v + __ffsll((long long)hit) - 1;
         }
 #pragma unroll
         for (int v = 0; v < V; ++v)

@@ -36,8 +36,7 @@ template <bool FP8, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
                                                    const HandleRecord* __restrict__ meta,
                                                    const int32_t* __restrict__ rank_recv_off,
-                                                   uint4* __restrict__ out, int P, int E, int Ep, int L,
-                                                   int slices) {
+                                                   uint4* __restrict__ out, int P, int E, int Ep, int L) {
     const int q = blockIdx.x;
     const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
@@ -88,7 +87,7 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
     launch_kernel(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
                        reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
-                       d.P, d.E, d.Ep, L, slices);
+                       d.P, d.E, d.Ep, L);
     return hipGetLastError();
 }
 
