@@ -33,11 +33,13 @@ KERNEL_SOURCES = {
     "route_topk": "route.hip", "count": "count.hip", "scan": "count.hip", "pack": "pack.hip",
     "exchange": "exchange.hip", "stub": "stub.hip", "reverse_exchange": "exchange.hip", "reduce": "reduce.hip",
     "pack_direct": "pack.hip", "reduce_direct": "reduce.hip", "count_pack": "pack.hip", "count_pack_direct": "pack.hip",
+    "allgather": "pack.hip", "handles": "pack.hip", "count_handles": "pack.hip", "select": "exchange.hip",
 }
 PHASE_OF = {
     "route_topk": "route", "count": "dispatch", "scan": "dispatch", "pack": "dispatch", "exchange": "dispatch",
     "stub": "expert_stub", "reverse_exchange": "combine", "reduce": "combine",
     "pack_direct": "dispatch", "reduce_direct": "combine", "count_pack": "dispatch", "count_pack_direct": "dispatch",
+    "allgather": "dispatch", "handles": "dispatch", "count_handles": "dispatch", "select": "dispatch",
 }
 
 
@@ -63,6 +65,10 @@ def kernel_bytes(w) -> dict:
         "reduce_direct": Na * 2 * H + 2 * H * T,    # reads the expert output through the handle
         "count_pack": count + pack,                  # small problems: the pack kernel counts by itself
         "count_pack_direct": count + pack,
+        "allgather": 2 * H * T + w.num_ranks * T * D,   # every rank's copy of every token
+        "handles": 8 * Na,                           # positions and records only (metadata)
+        "count_handles": count,
+        "select": 2 * Na * D,                        # each rank's pick from its own copy
     }
 
 
@@ -98,7 +104,8 @@ def load_traffic(config: str, kernel: str):
 
 KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the path
     ("route_topk", "route_topk"), ("count_scan_single_kernel", "count"), ("count_kernel", "count"),
-    ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"), ("reverse_exchange_", "reverse_exchange"),
+    ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"),
+    ("allgather_kernel", "allgather"), ("handle_kernel", "handles"), ("select_kernel", "select"), ("reverse_exchange_", "reverse_exchange"),
     ("exchange_kernel", "exchange"), ("stub_kernel", "stub"), ("reduce_kernel", "reduce"),
 )
 
@@ -222,6 +229,8 @@ def main():
     ap.add_argument("--mode", default="base", choices=["base", "direct"],
                     help="base: pack into send buffers + exchange copies; direct: pack straight into the "
                          "receive rows and reduce straight from the expert output")
+    ap.add_argument("--ranks", type=int, default=0,
+                    help="comparison runs only: the workload with this many logical ranks instead of its own")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
@@ -252,6 +261,9 @@ def main():
     from combine_router_softmax_expert_amd import workloads as wl
 
     w = wl.WORKLOADS[args.config]
+    if args.ranks:
+        w = wl.custom(f"{w.name}-as-ep{args.ranks}", args.ranks, w.tokens, w.num_experts, w.top_k, w.hidden,
+                      w.dispatch_dtype, w.seed, w.zipf)
     inp = wl.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -315,6 +327,23 @@ def main():
     B.moe_timing_begin(ctx)
     step(other)                      # once, for the names of the kernels it runs
     kt_other = B.moe_timing_end(ctx)
+    step()   # leave the buffers as the measured form wrote them
+
+    # the all-gather dispatcher (with the base combine) on the same data
+    gathered, gathered_scales = ctx.allocate_gathered(dev)
+
+    def allgather_dc():
+        h = B.moe_dispatch_allgather(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], gathered,
+                                     gathered_scales, bufs["recv"], bufs["recv_scales"], stream)
+        B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+
+    for _ in range(args.warmup):
+        allgather_dc()
+    ag_dc_ms = timed(allgather_dc, args.steps)
+    B.moe_timing_begin(ctx)
+    timed(allgather_dc, args.steps)
+    kt_ag = B.moe_timing_end(ctx)
+    del gathered, gathered_scales
     step()   # leave the buffers as the measured form wrote them
 
     # per-step times with the caches flushed before each step (a 1 GiB write)
@@ -432,6 +461,11 @@ def main():
             "dispatch_combine_ms": round(other_dc_ms, 5),
             "dispatch_combine_tokens_per_s": round(T / (other_dc_ms * 1e-3), 1),
             "dispatch_combine_gbps": round(other_dc_bytes / (other_dc_ms * 1e-3) / 1e9, 1),
+        },
+        "allgather_dispatch": {
+            "dispatch_combine_ms": round(ag_dc_ms, 5), "dispatch_combine_tokens_per_s": round(T / (ag_dc_ms * 1e-3), 1),
+            "algorithmic_bytes": sum(kb[n] for n in kt_ag if PHASE_OF[n] in ("dispatch", "combine")),
+            "kernels_ms": {n: round(v[1] / v[0], 5) for n, v in kt_ag.items()},
         },
         "graph_replay": graph,
         "micro_batches": micro,

@@ -68,6 +68,7 @@ def _load():
         "moe_combine": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
         "moe_dispatch_direct": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_combine_direct": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
+        "moe_dispatch_allgather": (I32, [P, P, P, P, P, SZ, P, P, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_dispatch_send": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_dispatch_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
         "moe_combine_send": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P]),
@@ -169,6 +170,13 @@ class Context:
         except Exception:
             pass
 
+    def allocate_gathered(self, device="cuda"):
+        """The all-gather dispatcher's per-rank copies of every token (rows and FP8 scales)."""
+        import torch
+        rows = self.P * self.T
+        return (torch.empty((rows, self.row_bytes), dtype=torch.uint8, device=device),
+                torch.empty((rows, self.scales_per_row), dtype=torch.float32, device=device) if self.fp8 else None)
+
     def allocate(self, device="cuda"):
         """Caller-owned device buffers of the sizes the calls expect (torch.empty: contents undefined)."""
         import torch
@@ -262,6 +270,25 @@ def moe_combine_direct(ctx: Context, handle: MoeHandle, expert_out, topk_w, y, s
                                   _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
                                   _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
            "moe_combine_direct")
+
+
+def moe_dispatch_allgather(ctx: Context, x, topk_ids, topk_w, workspace, gathered, gathered_scales, recv_buf,
+                           recv_scales, stream=None) -> MoeHandle:
+    import torch
+    T, H, k, Na, P = ctx.T, ctx.H, ctx.k, ctx.num_assignments, ctx.P
+    rb, nb = ctx.row_bytes, ctx.scales_per_row
+    h = MoeHandle()
+    ws = _ptr(workspace, None, ctx.workspace_bytes, "workspace")
+    _check(lib.moe_dispatch_allgather(ctx.handle_ptr, _ptr(x, (torch.bfloat16, torch.int16), 2 * T * H, "x"),
+                                      _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                                      _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                      ws, workspace.numel() * workspace.element_size(),
+                                      _ptr(gathered, None, P * T * rb, "gathered"),
+                                      _ptr(gathered_scales, torch.float32, 4 * P * T * nb, "gathered_scales"),
+                                      _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                                      _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"),
+                                      ctypes.byref(h), _stream(stream)), "moe_dispatch_allgather")
+    return h
 
 
 def moe_dispatch_send(ctx: Context, x, topk_ids, topk_w, workspace, send_buf, send_scales, stream=None) -> MoeHandle:

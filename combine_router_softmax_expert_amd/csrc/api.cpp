@@ -384,6 +384,40 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
     return MOE_OK;
 }
 
+moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                                  void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
+                                  void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const moe::Dims d = ctx->d;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.fp8 ? (d.T > 0 && (!gathered_scales || !recv_scales)) : (gathered_scales || recv_scales))
+        return MOE_ERR_INVALID_ARG;
+
+    const moe::Workspace ws = carve(ctx, workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d.T > 0) {
+        moe_status s = validate_ids(ctx, d, topk_ids, ws, st);
+        if (s != MOE_OK) return s;
+        s = launch(ctx, "allgather", st, [&] { return moe::launch_allgather(d, x, gathered, gathered_scales, st); });
+        const bool fused = moe::pack_counts(d);
+        if (s == MOE_OK && !fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
+        if (s == MOE_OK)
+            s = launch(ctx, fused ? "count_handles" : "handles", st,
+                       [&] { return moe::launch_pack_handles(d, topk_ids, topk_w, ws, st); });
+        if (s == MOE_OK)
+            s = launch(ctx, "select", st, [&] {
+                return moe::launch_select(d, ws, topk_ids, gathered, gathered_scales, recv_buf, recv_scales, st);
+            });
+        if (s != MOE_OK) return s;
+    }
+    ctx->workspace = workspace;
+    fill_handle(ctx, ws, handle, false);
+    ctx->received = ctx->generation;
+    return MOE_OK;
+}
+
 moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf, const float* recv_scales,
                            uint16_t* expert_out, void* stream) {
     if (!ctx) return MOE_ERR_INVALID_ARG;

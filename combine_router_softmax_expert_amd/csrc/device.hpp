@@ -138,6 +138,19 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Rank whose receive region holds receive row q: the number of region starts
+// rank_recv_off[0..P] that are <= q, less one (a ballot per 64 ranks).
+__device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_off, int P, int q) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int count = 0;
+    for (int r0 = 0; r0 <= P; r0 += kWave) {
+        const int r = r0 + lane;
+        const bool le = r <= P && rank_recv_off[r] <= q;
+        count += __popcll(__ballot(le));
+    }
+    return count - 1;
+}
+
 // Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
 // `tmp` needs blockDim.x / 64 + 1 ints of LDS.  Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {

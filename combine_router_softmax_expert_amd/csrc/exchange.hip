@@ -77,7 +77,77 @@ __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint
     if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
 }
 
+// The all-gather dispatcher's local pick ("Expert Parallel: MoE Token ...",
+// section "为什么不用 AllGather 收集所有 token": each rank picks its own
+// assignments out of the gathered tokens): receive row q of rank r takes the
+// token (s, i) its record names from rank r's own copy, row r*T + s*T/P + i,
+// with its FP8 scales.
+template <bool NT>
+__global__ __launch_bounds__(512) void select_kernel(const uint4* __restrict__ gathered,
+                                                     const float* __restrict__ gathered_scales,
+                                                     uint4* __restrict__ recv, float* __restrict__ recv_scales,
+                                                     const HandleRecord* __restrict__ recv_meta,
+                                                     const int32_t* __restrict__ rank_recv_off, int P, int T, int Tp,
+                                                     int L, int nb) {
+    const int q = blockIdx.x;
+    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+    const int r = owner_rank(rank_recv_off, P, q);
+    const HandleRecord m = recv_meta[q];
+    const size_t src = (size_t)r * T + (size_t)m.src_rank * Tp + m.src_token;
+    if (u < L) st16<NT>(&recv[(size_t)q * L + u], ld16<NT>(&gathered[src * L + u]));
+    if (blockIdx.y == 0)
+        for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = gathered_scales[src * nb + x];
+}
+
+// Source-walking form of the same pick, for when every rank's copy is mostly
+// needed (P <= 2k): workgroup (r, t) loads row t of rank r's copy at once, then
+// stores it to the receive row of every slot of token t whose expert lives on
+// rank r (ids and positions load alongside the row, so no load waits on another).
+template <bool NT>
+__global__ __launch_bounds__(512) void select_scatter_kernel(const uint4* __restrict__ gathered,
+                                                             const float* __restrict__ gathered_scales,
+                                                             uint4* __restrict__ recv, float* __restrict__ recv_scales,
+                                                             const int32_t* __restrict__ ids,
+                                                             const int32_t* __restrict__ recv_pos, int T, int Ep, int k,
+                                                             int L, int nb) {
+    const int g = blockIdx.x;                  // row r*T + t of the gathered copies
+    const int r = g / T, t = g - r * T;
+    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (u < L) v = ld16<NT>(&gathered[(size_t)g * L + u]);
+    for (int j = 0; j < k; ++j) {
+        const int a = t * k + j;
+        if (ids[a] / Ep != r) continue;        // uniform: the same slot in every lane
+        const int q = recv_pos[a];
+        if (u < L) st16<NT>(&recv[(size_t)q * L + u], v);
+        if (blockIdx.y == 0)
+            for (int x = threadIdx.x; x < nb; x += blockDim.x)
+                recv_scales[(size_t)q * nb + x] = gathered_scales[(size_t)g * nb + x];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids, const void* gathered,
+                         const float* gathered_scales, void* recv, float* recv_scales, hipStream_t st) {
+    if (d.Na == 0) return hipSuccess;
+    const int L = d.row_units;
+    const int B = pick_block(L);
+    const int slices = (L + B - 1) / B;
+    const bool nt = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
+    if (d.P <= 2 * d.k) {
+        auto kernel = nt ? select_scatter_kernel<true> : select_scatter_kernel<false>;
+        launch_kernel(kernel, dim3((unsigned)(d.P * d.T), (unsigned)slices), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv),
+                      recv_scales, ids, ws.recv_pos, d.T, d.Ep, d.k, L, d.scales);
+        return hipGetLastError();
+    }
+    auto kernel = nt ? select_kernel<true> : select_kernel<false>;
+    launch_kernel(kernel, dim3((unsigned)d.Na, (unsigned)slices), dim3(B), 0, st,
+                  reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv), recv_scales,
+                  reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, d.P, d.T, d.Tp, L, d.scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
                            void* recv, float* recv_scales, hipStream_t st) {

@@ -80,6 +80,14 @@ hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st);
 // direct: rows, scales and records go straight to their receive rows (dst = the receive buffer)
 hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w,
                        const Workspace& ws, void* dst, float* dst_scales, bool direct, hipStream_t st);
+// All-gather dispatcher: every rank's copy of every token's dispatched row
+// (gathered = [P*T][row], scales [P*T][H/128]); the receive-side positions and
+// records without rows; each rank's pick of its receive rows from its copy.
+hipError_t launch_allgather(const Dims& d, const uint16_t* x, void* gathered, float* gathered_scales, hipStream_t st);
+hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w, const Workspace& ws,
+                               hipStream_t st);
+hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids, const void* gathered,
+                         const float* gathered_scales, void* recv, float* recv_scales, hipStream_t st);
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
                            void* recv, float* recv_scales, hipStream_t st);
 hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales,

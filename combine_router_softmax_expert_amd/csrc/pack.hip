@@ -48,6 +48,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxIdsPerThread = 16;   // expert ids a thread of the counting form keeps in registers
+constexpr int kMaxRanksPerStore = 32;  // row copies the all-gather writes per pass
 
 // The token's row, loaded before anything else so its latency overlaps the
 // position work (FP8 reads 32 bytes of bf16 per 16-byte output unit).
@@ -194,6 +195,48 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
                              recv_pos);
 }
 
+// Positions and receive-side handle records only (no rows), one thread per
+// assignment, for dispatchers that move the rows another way (the all-gather
+// dispatcher of "Expert Parallel: MoE Token ...", section "为什么不用 AllGather
+// 收集所有 token").
+__global__ __launch_bounds__(256) void handle_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                     const int32_t* __restrict__ bucket_rank,
+                                                     const int32_t* __restrict__ send_off,
+                                                     const int32_t* __restrict__ recv_off,
+                                                     HandleRecord* __restrict__ recv_meta,
+                                                     int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
+                                                     int Na, int Tp, int E, int Ep, int k) {
+    const int a = blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= Na) return;
+    const int t = a / k, s = t / Tp;
+    const int e = ids[a];
+    const int br = bucket_rank[a];
+    const int p = send_off[s * E + e] + br;
+    const int q = recv_off[s * E + e] + br;
+    write_handle<true>(a, t, s, Tp, a - t * k, e, Ep, p, q, w[a], recv_meta, nullptr, nullptr, send_pos, recv_pos);
+}
+
+// All-gather of the tokens ("Expert Parallel: MoE Token ...", section "为什么不用
+// AllGather 收集所有 token": every rank gathers all tokens, then picks out its own
+// assignments): token t's row, in its dispatched form (the FP8 codes and
+// scales computed once), lands in row r*T + t of every rank r's copy.
+template <bool FP8, bool NTL, bool NTS>
+__global__ __launch_bounds__(512) void allgather_kernel(const uint4* __restrict__ x, uint4* __restrict__ gathered,
+                                                        float* __restrict__ gathered_scales, int T, int P, int L) {
+    __shared__ int32_t pos[kMaxRanksPerStore];
+    const int t = blockIdx.x;
+    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+    uint4 xa, xb;
+    load_row<FP8, NTL>(x, t, L, u, xa, xb);
+    for (int r0 = 0; r0 < P; r0 += kMaxRanksPerStore) {   // copies in groups of the position table
+        const int n = min(kMaxRanksPerStore, P - r0);
+        if ((int)threadIdx.x < n) pos[threadIdx.x] = (r0 + threadIdx.x) * T + t;
+        lds_barrier();
+        store_rows<FP8, NTS>(xa, xb, pos, n, L, u, gathered, gathered_scales);
+        lds_barrier();
+    }
+}
+
 // Counts and offsets of source rank s for the handle (one workgroup of the
 // counting form per rank): LDS histograms of all ids, of the ids of ranks
 // below s and of rank s's ids, then one exclusive scan over the experts of
@@ -271,7 +314,7 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
 // with c = #{t0*k <= a < t*k : id_a = e} (earlier tokens of the same block).
 // Four LDS histograms of the ids (all, before t0, rank s, rank s before t0)
 // and one prefix sum give the first two terms of both.
-template <bool FP8, bool DIRECT, int MI, int TPB>
+template <bool FP8, bool DIRECT, int MI, int TPB, bool ROWS = true>
 __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
                                                          const float* __restrict__ w, uint4* __restrict__ dst,
                                                          float* __restrict__ dst_scales,
@@ -316,7 +359,9 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     __builtin_amdgcn_sched_barrier(0);
     uint4 xa[TPB], xb[TPB];
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) load_row<FP8, false>(x, min(t0 + i, T - 1), L, u, xa[i], xb[i]);
+    for (int i = 0; i < TPB; ++i) {
+        if (ROWS) load_row<FP8, false>(x, min(t0 + i, T - 1), L, u, xa[i], xb[i]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     extern __shared__ __align__(16) int32_t hist[];   // [5][E]: all, before t0, rank s, rank s before t0, prefix
@@ -368,7 +413,7 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < TPB; ++i)
-        if (i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
+        if (ROWS && i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
     if (tid < nslots && slice == 0) {
         const int t = t0 + tid / k;
         write_handle<DIRECT>(t0k + tid, t, s, Tp, tid % k, my_e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send,
@@ -453,6 +498,48 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
                        reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
                        reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
                        ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w, const Workspace& ws,
+                               hipStream_t st) {
+    if (d.T == 0) return hipSuccess;
+    HandleRecord* meta = reinterpret_cast<HandleRecord*>(ws.recv_meta);
+    if (pack_counts(d)) {
+        const int B = pick_block(d.row_units);
+        const int mi = ids_per_thread(d.Na, B);
+        const int tpb = tokens_per_block(d);
+        auto pick = [&](auto m) {
+            constexpr int MI = decltype(m)::value;
+            return tpb == 4 ? count_pack_kernel<false, true, MI, 4, false>
+                 : tpb == 2 ? count_pack_kernel<false, true, MI, 2, false> : count_pack_kernel<false, true, MI, 1, false>;
+        };
+        auto kernel = mi == 4 ? pick(std::integral_constant<int, 4>{})
+                    : mi == 8 ? pick(std::integral_constant<int, 8>{}) : pick(std::integral_constant<int, 16>{});
+        const size_t lds = 4 * 5 * (size_t)d.E;
+        const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
+        launch_kernel(kernel, dim3(blocks, 1u), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
+                      static_cast<uint4*>(nullptr), static_cast<float*>(nullptr), meta, ws.send_to_recv,
+                      ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C, ws.expert_off, ws.rank_recv_off,
+                      ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P, d.row_units);
+        return hipGetLastError();
+    }
+    const unsigned blocks = (unsigned)((d.Na + 255) / 256);
+    launch_kernel(handle_kernel, dim3(blocks), dim3(256), 0, st, ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
+                  meta, ws.send_pos, ws.recv_pos, (int)d.Na, d.Tp, d.E, d.Ep, d.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_allgather(const Dims& d, const uint16_t* x, void* gathered, float* gathered_scales, hipStream_t st) {
+    if (d.T == 0) return hipSuccess;
+    const int L = d.row_units;
+    const int B = pick_block(L);
+    const int slices = (L + B - 1) / B;
+    const bool nt = streaming(d, 2LL * d.H * d.T + (long long)d.P * d.T * (16LL * L + 4LL * d.scales));
+    auto kernel = d.fp8 ? (nt ? allgather_kernel<true, true, false> : allgather_kernel<true, false, false>)
+                        : (nt ? allgather_kernel<false, true, false> : allgather_kernel<false, false, false>);
+    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x),
+                  reinterpret_cast<uint4*>(gathered), gathered_scales, d.T, d.P, L);
     return hipGetLastError();
 }
 

@@ -16,18 +16,6 @@
 namespace moe {
 namespace {
 
-// Rank whose receive region holds row q: the number of region starts <= q, less one.
-__device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_off, int P, int q) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int count = 0;
-    for (int r0 = 0; r0 <= P; r0 += kWave) {
-        const int r = r0 + lane;
-        const bool le = r <= P && rank_recv_off[r] <= q;
-        count += __popcll(__ballot(le));
-    }
-    return count - 1;
-}
-
 // bf16 rows: one lane per 16-byte unit in and out.  e4m3 rows: one lane per 16
 // codes (a 16-byte load) and two 16-byte stores; with half-width (8-byte) code
 // loads instead, the kernel ran ~25% slower on gfx950, and the split stores must

@@ -226,6 +226,25 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
 moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                               const float* topk_w, uint16_t* y, void* stream);
 
+/* ---- the all-gather dispatcher --------------------------------------------- */
+
+/* Dispatch by all-gather ([EP] "为什么不用 AllGather 收集所有 token": every rank
+ * gathers all tokens and picks out the assignments of its own experts; no
+ * variable-length point-to-point permutation, but every token reaches every
+ * rank, so it pays only with few ranks, a large top-k or a tiny batch).  The
+ * all-gather writes every token's dispatched row (FP8 codes and scales
+ * computed once per token) into each rank's copy; each rank then picks its
+ * receive rows from its own copy.  Receive rows, scales, records, counts,
+ * offsets and positions equal moe_dispatch's; the handle's send_meta is NULL
+ * and it serves moe_expert_stub, moe_combine and moe_combine_direct.
+ *   gathered         [P*T][row] out: row r*T + t holds token t in rank r's copy
+ *   gathered_scales  fp32 [P*T][H/128] out (e4m3 only, else NULL)
+ * Other arguments as moe_dispatch.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                                  void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
+                                  void* recv_buf, float* recv_scales, moe_handle* handle, void* stream);
+
 /* ---- split phases ([PPLX]: dispatch and combine each run as a send half and
  * a receive half, so that other work can run in between; [A2A] 7: overlap pays
  * only when there is independent work to hide the exchange behind) --------- */
@@ -267,8 +286,9 @@ const char* moe_last_error(void);
  * events, writes up to `max` records (one per kernel name, in first-launch
  * order) and returns how many kernels were seen in *count.  Kernel names:
  * route_topk, count, scan, pack, count_pack (the pack kernel counting by
- * itself, small problems), exchange, stub, reverse_exchange, reduce, and
- * pack_direct, count_pack_direct, reduce_direct for the direct forms. */
+ * itself, small problems), exchange, stub, reverse_exchange, reduce;
+ * pack_direct, count_pack_direct, reduce_direct for the direct forms;
+ * allgather, handles or count_handles, select for the all-gather dispatcher. */
 moe_status moe_timing_begin(moe_ctx* ctx);
 moe_status moe_timing_end(moe_ctx* ctx, moe_kernel_time* out, int32_t max, int32_t* count);
 

@@ -23,9 +23,11 @@ def _ws_view(ws, base_ptr, ptr, nbytes, dtype):
     return ws[off:off + nbytes].cpu().numpy().view(dtype)
 
 
-def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, read_payload=True, direct=False):
+def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, read_payload=True, direct=False,
+            allgather=False):
     """Run route (unless ids/w are given), dispatch, stub and combine on cuda:0
-    (the direct forms if asked); returns numpy copies of every output."""
+    (the direct forms, or the all-gather dispatch with the base combine, if
+    asked); returns numpy copies of every output."""
     import torch
     from combine_router_softmax_expert_amd import binding as B
     from oracle.oracle import META_DTYPE
@@ -33,6 +35,8 @@ def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, re
     P, T, E, k, H = shape.P, shape.T, shape.E, shape.k, shape.H
     ctx = B.Context(P, T // P, E, k, H, shape.fp8)
     bufs = ctx.allocate()
+    if allgather:
+        bufs["gathered"], bufs["gathered_scales"] = ctx.allocate_gathered()
     if sentinel:
         for key, t in bufs.items():
             if t is not None and key not in ("workspace",):
@@ -48,7 +52,10 @@ def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, re
     for _ in range(repeat):
         if ids is None:
             B.moe_route_topk(ctx, ld, bufs["topk_ids"], bufs["topk_w"])
-        if direct:
+        if allgather:
+            h = B.moe_dispatch_allgather(ctx, xd, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"],
+                                         bufs["gathered"], bufs["gathered_scales"], bufs["recv"], bufs["recv_scales"])
+        elif direct:
             h = B.moe_dispatch_direct(ctx, xd, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
                                       bufs["recv_scales"])
         else:
@@ -75,18 +82,22 @@ def run_gpu(shape, x, logits=None, ids=None, w=None, sentinel=True, repeat=1, re
         "recv_off": _ws_view(ws, base, h.recv_offsets, 4 * E * P, np.int32).reshape(P, E).T,
         "send_pos": _ws_view(ws, base, h.send_pos, 4 * Na, np.int32).reshape(T, k),
         "recv_pos": _ws_view(ws, base, h.recv_pos, 4 * Na, np.int32).reshape(T, k),
-        "send_meta": None if direct else _ws_view(ws, base, h.send_meta, 16 * Na, META_DTYPE),
+        "send_meta": None if (direct or allgather) else _ws_view(ws, base, h.send_meta, 16 * Na, META_DTYPE),
         "recv_meta": _ws_view(ws, base, h.recv_meta, 16 * Na, META_DTYPE),
     }
     if read_payload:
         out.update({
-            "send_rows": None if direct else bufs["send"].cpu().numpy(), "recv_rows": bufs["recv"].cpu().numpy(),
-            "send_scales": bufs["send_scales"].cpu().numpy() if shape.fp8 and not direct else None,
+            "send_rows": None if (direct or allgather) else bufs["send"].cpu().numpy(),
+            "recv_rows": bufs["recv"].cpu().numpy(),
+            "send_scales": bufs["send_scales"].cpu().numpy() if shape.fp8 and not (direct or allgather) else None,
             "recv_scales": bufs["recv_scales"].cpu().numpy() if shape.fp8 else None,
             "expert_out": bufs["expert_out"].view(torch.int16).cpu().numpy().view(np.uint16),
             "comb": None if direct else bufs["comb"].view(torch.int16).cpu().numpy().view(np.uint16),
             "y": bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16),
         })
+        if allgather:
+            out["gathered"] = bufs["gathered"].cpu().numpy()
+            out["gathered_scales"] = bufs["gathered_scales"].cpu().numpy() if shape.fp8 else None
     else:
         out["_bufs"] = bufs
     out["_ctx"] = ctx

@@ -211,3 +211,22 @@ def test_split_phases_validate_arguments(b):
     assert b.lib.moe_combine_send(h, ctypes.byref(b.MoeHandle()), fake, fake, None) == -4
     assert b.lib.moe_combine_recv(h, ctypes.byref(b.MoeHandle()), fake, fake, fake, None) == -4
     b.lib.moe_ctx_destroy(h)
+
+
+def test_allgather_dispatch_validates_arguments(b):
+    st, h = _create(b)
+    fake = ctypes.c_void_p(1 << 20)
+    ws = b.lib.moe_workspace_bytes(h)
+    hd = b.MoeHandle()
+    A = b.lib.moe_dispatch_allgather
+    assert A(h, fake, fake, fake, fake, ws, None, None, fake, None, ctypes.byref(hd), None) == -1    # no gathered buffer
+    assert A(h, fake, fake, fake, fake, ws, fake, fake, fake, None, ctypes.byref(hd), None) == -1    # bf16 takes no scales
+    assert A(h, fake, fake, fake, fake, ws - 1, fake, None, fake, None, ctypes.byref(hd), None) == -3
+    assert A(h, fake, fake, fake, fake, ws, fake, None, fake, None, None, None) == -1
+    b.lib.moe_ctx_destroy(h)
+    st, h0 = _create(b, Tp=0)
+    h1 = b.MoeHandle()
+    assert b.lib.moe_dispatch_allgather(h0, None, None, None, fake, b.lib.moe_workspace_bytes(h0), None, None, None,
+                                        None, ctypes.byref(h1), None) == 0
+    assert not h1.send_meta and b.lib.moe_combine(h0, ctypes.byref(h1), None, None, None, None, None) == 0
+    b.lib.moe_ctx_destroy(h0)

@@ -17,14 +17,14 @@ from gpu_helpers import (assert_integer_parts_equal, assert_weights_close, asser
 pytestmark = pytest.mark.gpu
 
 
-def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label="", direct=False):
+def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label="", direct=False, allgather=False):
     log(f"[parity] {label} P={sh.P} T={sh.T} E={sh.E} k={sh.k} H={sh.H} fp8={sh.fp8} "
         f"{'route' if ids is None else 'given ids'}{' direct' if direct else ''}")
     if ids is None:
         o_ids, o_w = orc.route(sh, logits)
     else:
         o_ids, o_w = ids, w
-    g = run_gpu(sh, x, logits=logits, ids=ids, w=w, direct=direct)
+    g = run_gpu(sh, x, logits=logits, ids=ids, w=w, direct=direct, allgather=allgather)
     assert np.array_equal(g["ids"], o_ids)
     if ids is None:
         assert_weights_close(g["w"], o_w)
@@ -42,6 +42,19 @@ def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label="", direct=Fal
     assert_y_close(g["y"], o["y32"])
     if np.array_equal(g["w"], o_w):
         assert np.array_equal(g["y"], o["y"])
+    if allgather:
+        # every rank's copy holds every token in its dispatched form
+        if sh.fp8:
+            rows = [orc.quantize_row(sh.H, x[t]) for t in range(sh.T)]
+            codes = np.stack([r[0] for r in rows])
+            scales = np.stack([r[1] for r in rows])
+        else:
+            codes = np.ascontiguousarray(x).view(np.uint8).reshape(sh.T, 2 * sh.H)
+        for r in range(sh.P):
+            assert np.array_equal(g["gathered"][r * sh.T:(r + 1) * sh.T], codes), ("gathered rows", r)
+            if sh.fp8:
+                assert np.array_equal(g["gathered_scales"][r * sh.T:(r + 1) * sh.T].view(np.uint32),
+                                      scales.view(np.uint32)), ("gathered scales", r)
     return g, o
 
 
@@ -71,6 +84,14 @@ def test_workload_parity_separate_count(orc, monkeypatch, name, direct):
     inp = wl.make_inputs(w)
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} separate count",
                  direct=direct)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_workload_parity_allgather(orc, name):
+    # every rank gathers every token and picks its own assignments; same receive side
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} allgather", allgather=True)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
@@ -171,16 +192,19 @@ EDGE = [
 
 @pytest.mark.parametrize("policy,count,direct", [("auto", "auto", False), ("streaming", "auto", False),
                                                  ("auto", "auto", True), ("auto", "separate", False),
-                                                 ("auto", "fused", True)])
+                                                 ("auto", "fused", True), ("auto", "auto", "allgather"),
+                                                 ("streaming", "separate", "allgather")])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, count, direct):
     monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
     monkeypatch.setenv("MOE_EP_COUNT_PATH", count)
+    allgather = direct == "allgather"
+    direct = direct is True
     sh = orc.Shape(P, P * Tp, E, k, H, fp8)
     seed = zlib.crc32(name.encode())
     x = wl.make_hidden(seed, sh.T, H)
     logits = wl.make_logits(seed, sh.T, E)
-    _full_parity(orc, sh, x, logits=logits, label=name, direct=direct)
+    _full_parity(orc, sh, x, logits=logits, label=name, direct=direct, allgather=allgather)
 
 
 def test_all_tokens_to_one_remote_rank_and_empty_experts(orc):
