@@ -112,17 +112,18 @@ def test_workload_parity_with_oracle_routing(orc):
     assert np.array_equal(g["y"], o["y"])
 
 
-@pytest.mark.parametrize("direct", [False, True])
-def test_skewed_workload_full_size_sampled(orc, direct):
+@pytest.mark.parametrize("mode", ["base", "direct", "allgather"])
+def test_skewed_workload_full_size_sampled(orc, mode):
     # c5 at its full size, in the launch configuration the benchmark times: all
     # routing, counts, offsets, positions and handle records in full; payload,
     # stub and combine on sampled tokens that the oracle computes one by one
     w = wl.WORKLOADS["c5"]
     sh = orc.Shape.of(w)
-    log(f"[parity] c5 full size{' direct' if direct else ''}, generating inputs")
+    direct, allgather = mode == "direct", mode == "allgather"
+    log(f"[parity] c5 full size {mode}, generating inputs")
     inp = wl.make_inputs(w)
     o_ids, o_w = orc.route(sh, inp["logits"])
-    g = run_gpu(sh, inp["x"], logits=inp["logits"], direct=direct)
+    g = run_gpu(sh, inp["x"], logits=inp["logits"], direct=direct, allgather=allgather)
     assert np.array_equal(g["ids"], o_ids)
     assert_weights_close(g["w"], o_w)
     o = orc.dispatch(sh, inp["x"], o_ids, o_w, payload=False)
@@ -138,12 +139,16 @@ def test_skewed_workload_full_size_sampled(orc, direct):
         for j in range(sh.k):
             p, qq = o["send_pos"][t, j], o["recv_pos"][t, j]
             assert np.array_equal(g["recv_rows"][qq], q) and np.array_equal(g["recv_scales"][qq], sc)
-            if not direct:
+            if mode == "base":
                 assert np.array_equal(g["send_rows"][p], q) and np.array_equal(g["send_scales"][p], sc)
+            if allgather:               # the token in every rank's copy
+                for rr in range(sh.P):
+                    assert np.array_equal(g["gathered"][rr * sh.T + t], q)
+                    assert np.array_equal(g["gathered_scales"][rr * sh.T + t], sc)
             e = int(o_ids[t, j])
             stub_rows[r, j] = orc.stub_row(sh, e, q, sc)
             assert np.array_equal(g["expert_out"][qq], stub_rows[r, j])
-            if not direct:
+            if not direct:              # the base combine also serves the all-gather dispatch
                 assert np.array_equal(g["comb"][t * sh.k + j], stub_rows[r, j])
     red = orc.reduce_tokens(sh, tokens, stub_rows, o_w)
     assert_y_close(g["y"][tokens], red["y32"])
