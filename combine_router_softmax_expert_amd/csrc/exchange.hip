@@ -10,10 +10,10 @@
 // receive row q goes to combine row (s*T/P + i)*k + j of the (s, i, j) its
 // record names, which is the row whose recv_pos is q.
 //
-// Rows move whole with 16-byte loads and stores, one unit per thread (a second
-// load in flight before the stores runs 4x slower on gfx950 when the buffers
-// sit in the last-level cache); a workgroup slice covers a row or part of one,
-// so the permutation costs one index (or record) load per row.  Two forms:
+// Rows move whole with 16-byte loads and stores, one unit per thread (two or
+// four units, or two rows, per thread measured no faster on gfx950); a
+// workgroup slice covers a row or part of one, so the permutation costs one
+// index (or record) load per row.  Two forms:
 //  - temporal (buffers that stay in cache): walk the source rows and scatter;
 //  - streaming (large buffers): walk the destination rows in order, gather
 //    from the source, nontemporal loads and stores (~18% faster there).
