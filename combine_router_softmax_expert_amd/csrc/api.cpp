@@ -394,6 +394,7 @@ moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t
     if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf)) return MOE_ERR_INVALID_ARG;
     if (d.fp8 ? (d.T > 0 && (!gathered_scales || !recv_scales)) : (gathered_scales || recv_scales))
         return MOE_ERR_INVALID_ARG;
+    if ((long long)d.P * d.T >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;   // gathered rows are indexed in 32 bits
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);

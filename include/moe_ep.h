@@ -240,7 +240,8 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
  *   gathered         [P*T][row] out: row r*T + t holds token t in rank r's copy
  *   gathered_scales  fp32 [P*T][H/128] out (e4m3 only, else NULL)
  * Other arguments as moe_dispatch.
- * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_HIP; MOE_ERR_UNSUPPORTED
+ * when P * T >= 2^31 (the gathered rows). */
 moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                   void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
                                   void* recv_buf, float* recv_scales, moe_handle* handle, void* stream);

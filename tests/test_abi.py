@@ -224,6 +224,11 @@ def test_allgather_dispatch_validates_arguments(b):
     assert A(h, fake, fake, fake, fake, ws - 1, fake, None, fake, None, ctypes.byref(hd), None) == -3
     assert A(h, fake, fake, fake, fake, ws, fake, None, fake, None, None, None) == -1
     b.lib.moe_ctx_destroy(h)
+    st, hbig = _create(b, P=2, Tp=(1 << 30) - 1, E=2, k=1, H=8)     # P * T >= 2^31 gathered rows
+    assert st == 0
+    assert b.lib.moe_dispatch_allgather(hbig, fake, fake, fake, fake, b.lib.moe_workspace_bytes(hbig), fake, None,
+                                        fake, None, ctypes.byref(hd), None) == -2
+    b.lib.moe_ctx_destroy(hbig)
     st, h0 = _create(b, Tp=0)
     h1 = b.MoeHandle()
     assert b.lib.moe_dispatch_allgather(h0, None, None, None, fake, b.lib.moe_workspace_bytes(h0), None, None, None,
