@@ -105,7 +105,8 @@ def load_traffic(config: str, kernel: str):
 KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the path
     ("route_topk", "route_topk"), ("count_scan_single_kernel", "count"), ("count_kernel", "count"),
     ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"),
-    ("allgather_kernel", "allgather"), ("handle_kernel", "handles"), ("select_kernel", "select"), ("reverse_exchange_", "reverse_exchange"),
+    ("allgather_kernel", "allgather"), ("handle_kernel", "handles"), ("select_kernel", "select"),
+    ("select_scatter_kernel", "select"), ("reverse_exchange_", "reverse_exchange"),
     ("exchange_kernel", "exchange"), ("stub_kernel", "stub"), ("reduce_kernel", "reduce"),
 )
 
@@ -119,8 +120,10 @@ def path_kernel(rocprof_name: str):
         if frag in rocprof_name:
             i = DIRECT_TEMPLATE_ARG.get(k)
             if i is not None:
-                args = rocprof_name.split(frag + "<", 1)[1].split(">", 1)[0].split(",")
-                if args[i].strip() == "true":
+                args = [a.strip() for a in rocprof_name.split(frag + "<", 1)[1].split(">", 1)[0].split(",")]
+                if k == "count_pack" and len(args) > 4 and args[4] == "false":
+                    return "count_handles"          # the all-gather dispatcher's position pass (no rows)
+                if args[i] == "true":
                     k += "_direct"
             return k
     return None
@@ -143,14 +146,13 @@ def _counter_means(d: str, counter: str) -> dict:
 
 
 def ingest_counters(config: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
-                    copy_bytes: int, command: str):
+                    copy_bytes: int, command: str, path: str = os.path.join(ROOT, "profiles", "traffic.json")):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the path's kernels, each scaled by
-    known bytes / counter reading of a plain copy, into profiles/traffic.json."""
+    known bytes / counter reading of a plain copy, into ``path`` (profiles/traffic.json)."""
     fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
     cf = max(_counter_means(copy_fetch_dir, "FETCH_SIZE").values())
     cw = max(_counter_means(copy_write_dir, "WRITE_SIZE").values())
     f_fac, w_fac = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     rec = {}
     for name, kib in fetch.items():

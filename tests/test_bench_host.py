@@ -1,0 +1,89 @@
+"""Host logic of bench.py (no GPU): the single-GPU refusal, the algorithmic byte
+model against its closed form, rocprof kernel-name mapping and the counter
+calibration arithmetic."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from combine_router_softmax_expert_amd import workloads as wl  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT)
+    assert r.returncode == 2 and "exactly one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("name,total", [("c1", 1_835_008), ("c2", 91_750_400), ("c3", 325_713_920),
+                                        ("c4", 1_879_048_192), ("c5", 4_506_779_648)])
+def test_dispatch_combine_bytes_match_the_closed_form(name, total):
+    # 2HT + 3 N_a D + 3 N_a 2H + 2HT with D the dispatched row including FP8 scales
+    # (the totals of the byte model the measurement is defined by); the count's
+    # metadata bytes (8 N_a + 12 P E) are counted on top
+    w = wl.WORKLOADS[name]
+    kb = bench.kernel_bytes(w)
+    payload = kb["pack"] + kb["exchange"] + kb["reverse_exchange"] + kb["reduce"]
+    assert payload == total
+    H, T, Na = w.hidden, w.tokens, w.tokens * w.top_k
+    D = H + 4 * (H // 128) if w.dispatch_dtype != "bf16" else 2 * H
+    assert kb["pack_direct"] + kb["reduce_direct"] == 2 * H * T + Na * D + Na * 2 * H + 2 * H * T
+    assert kb["count_pack"] == kb["count"] + kb["pack"]
+
+
+def test_byte_model_example_payload():
+    # the logical payload of the byte-model workload: N_a * H * (1 + 2) bytes
+    w = wl.WORKLOADS["c3"]
+    assert w.tokens * w.top_k * w.hidden * (1 + 2) == 88_080_384
+
+
+@pytest.mark.parametrize("rocprof_name,kernel", [
+    ("void moe::(anonymous namespace)::count_pack_kernel<false, false, 4, 1, true>(x)", "count_pack"),
+    ("void moe::(anonymous namespace)::count_pack_kernel<true, true, 16, 2, true>(x)", "count_pack_direct"),
+    ("moe::(anonymous namespace)::pack_kernel<true, true, false, false>(x)", "pack"),
+    ("moe::(anonymous namespace)::pack_kernel<false, false, false, true>(x)", "pack_direct"),
+    ("reduce_kernel<true, true, true>(x)", "reduce_direct"), ("reduce_kernel<false, false, false>(x)", "reduce"),
+    ("reverse_exchange_gather_kernel(x)", "reverse_exchange"), ("reverse_exchange_scatter_kernel(x)",
+                                                                "reverse_exchange"),
+    ("exchange_kernel<true>(x)", "exchange"), ("count_scan_single_kernel(x)", "count"), ("scan_kernel(x)", "scan"),
+    ("allgather_kernel<true, false, false>(x)", "allgather"), ("select_scatter_kernel<false>(x)", "select"),
+    ("select_kernel<true>(x)", "select"), ("handle_kernel(x)", "handles"),
+    ("count_pack_kernel<false, true, 8, 1, false>(x)", "count_handles"),
+    ("route_topk_wave_kernel<4>(x)", "route_topk"), ("stub_kernel<true, true, false>(x)", "stub"),
+    ("at::native::vectorized_elementwise_kernel(x)", None),
+])
+def test_rocprof_names_map_to_path_steps(rocprof_name, kernel):
+    assert bench.path_kernel(rocprof_name) == kernel
+
+
+def _counter_csv(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_counter_ingestion_scales_by_the_copy_calibration(tmp_path):
+    copy_bytes = 1 << 30
+    # the copy reads FETCH_SIZE = half its bytes and WRITE_SIZE = all of them (KiB)
+    _counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copy", copy_bytes / 2048)])
+    _counter_csv(tmp_path / "cw", "WRITE_SIZE", [("copy", copy_bytes / 1024)])
+    name = "moe::(anonymous namespace)::exchange_kernel<false>(x)"
+    _counter_csv(tmp_path / "f", "FETCH_SIZE", [(name, 100.0), (name, 300.0)])   # mean 200 KiB
+    _counter_csv(tmp_path / "w", "WRITE_SIZE", [(name, 400.0)])
+    out = tmp_path / "traffic.json"
+    bench.ingest_counters("cX", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                          copy_bytes, "cmd", path=str(out))
+    rec = json.load(open(out))["cX"]["exchange"]
+    assert rec["fetch_bytes"] == 2 * 200 * 1024 and rec["write_bytes"] == 400 * 1024
+    assert rec["source_sha"] == bench.source_sha("exchange")
