@@ -236,6 +236,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
+    ap.add_argument("--core-only", action="store_true",
+                    help="only the timed steps, dispatch+combine and the per-kernel pass (for kernel traces: no "
+                         "other forms, micro-batches or graphs whose launches would mix into the statistics)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -320,37 +323,41 @@ def main():
     ms_with_events = timed(step, args.steps)
     kt = B.moe_timing_end(ctx)
 
-    # the other form of dispatch/combine on the same data, for comparison
-    other = not direct
-    for _ in range(args.warmup):
-        step(other)
-    other_ms = timed(lambda: step(other), args.steps)
-    other_dc_ms = timed(lambda: dispatch_combine(other), args.steps)
-    B.moe_timing_begin(ctx)
-    step(other)                      # once, for the names of the kernels it runs
-    kt_other = B.moe_timing_end(ctx)
-    step()   # leave the buffers as the measured form wrote them
+    extras = not args.core_only
+    other_ms = other_dc_ms = ag_dc_ms = None
+    kt_other, kt_ag, graph, micro = {}, {}, None, None
+    if extras:
+        # the other form of dispatch/combine on the same data, for comparison
+        other = not direct
+        for _ in range(args.warmup):
+            step(other)
+        other_ms = timed(lambda: step(other), args.steps)
+        other_dc_ms = timed(lambda: dispatch_combine(other), args.steps)
+        B.moe_timing_begin(ctx)
+        step(other)                      # once, for the names of the kernels it runs
+        kt_other = B.moe_timing_end(ctx)
+        step()   # leave the buffers as the measured form wrote them
 
-    # the all-gather dispatcher (with the base combine) on the same data
-    gathered, gathered_scales = ctx.allocate_gathered(dev)
+        # the all-gather dispatcher (with the base combine) on the same data
+        gathered, gathered_scales = ctx.allocate_gathered(dev)
 
-    def allgather_dc():
-        h = B.moe_dispatch_allgather(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], gathered,
-                                     gathered_scales, bufs["recv"], bufs["recv_scales"], stream)
-        B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+        def allgather_dc():
+            h = B.moe_dispatch_allgather(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], gathered,
+                                         gathered_scales, bufs["recv"], bufs["recv_scales"], stream)
+            B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
 
-    for _ in range(args.warmup):
-        allgather_dc()
-    ag_dc_ms = timed(allgather_dc, args.steps)
-    B.moe_timing_begin(ctx)
-    timed(allgather_dc, args.steps)
-    kt_ag = B.moe_timing_end(ctx)
-    del gathered, gathered_scales
-    step()   # leave the buffers as the measured form wrote them
+        for _ in range(args.warmup):
+            allgather_dc()
+        ag_dc_ms = timed(allgather_dc, args.steps)
+        B.moe_timing_begin(ctx)
+        timed(allgather_dc, args.steps)
+        kt_ag = B.moe_timing_end(ctx)
+        del gathered, gathered_scales
+        step()   # leave the buffers as the measured form wrote them
 
     # per-step times with the caches flushed before each step (a 1 GiB write)
     cold_ms = None
-    if not args.no_flush_run:
+    if extras and not args.no_flush_run:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         times = []
         for _ in range(min(args.steps, 30)):
@@ -364,58 +371,59 @@ def main():
         cold_ms = float(np.median(times))
         del flush
 
-    # the step captured once in a HIP graph and replayed (no per-call host work)
-    def graph_ms(direct):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            B.run_path(ctx, bufs, x, logits, None, direct=direct)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            B.run_path(ctx, bufs, x, logits, None, direct=direct)
-        for _ in range(args.warmup):
-            g.replay()
-        ms = timed(g.replay, args.steps)
-        del g
-        return ms
+    if extras:
+        # the step captured once in a HIP graph and replayed (no per-call host work)
+        def graph_ms(direct):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                B.run_path(ctx, bufs, x, logits, None, direct=direct)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                B.run_path(ctx, bufs, x, logits, None, direct=direct)
+            for _ in range(args.warmup):
+                g.replay()
+            ms = timed(g.replay, args.steps)
+            del g
+            return ms
 
-    graph = {}
-    for mode, d in (("base", False), ("direct", True)):
-        ms = graph_ms(d)
-        graph[mode] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
-    # two micro-batches through the split phases: the expert stage of one on a
-    # second stream overlaps the other's dispatch and combine (vs one stream)
-    fp8 = w.dispatch_dtype != "bf16"
-    parts = []
-    for c in range(2):
-        rows = torch.from_numpy(wl.micro_batch_rows(w.num_ranks, w.tokens_per_rank, 2, c)).to(dev)
-        cc = B.Context(w.num_ranks, w.tokens_per_rank // 2, w.num_experts, w.top_k, w.hidden, fp8)
-        parts.append((cc, cc.allocate(dev), x[rows].contiguous(), logits[rows].contiguous()))
+        graph = {}
+        for mode, d in (("base", False), ("direct", True)):
+            ms = graph_ms(d)
+            graph[mode] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
+        # two micro-batches through the split phases: the expert stage of one on a
+        # second stream overlaps the other's dispatch and combine (vs one stream)
+        fp8 = w.dispatch_dtype != "bf16"
+        parts = []
+        for c in range(2):
+            rows = torch.from_numpy(wl.micro_batch_rows(w.num_ranks, w.tokens_per_rank, 2, c)).to(dev)
+            cc = B.Context(w.num_ranks, w.tokens_per_rank // 2, w.num_experts, w.top_k, w.hidden, fp8)
+            parts.append((cc, cc.allocate(dev), x[rows].contiguous(), logits[rows].contiguous()))
 
-    def micro_batches_ms(same_stream):
-        """Eager launches: the host issues 12 calls per step, so at decode sizes this
-        measures the host; large problems measure the GPU."""
-        comm = torch.cuda.Stream()
-        compute = comm if same_stream else torch.cuda.Stream()
+        def micro_batches_ms(same_stream):
+            """Eager launches: the host issues 12 calls per step, so at decode sizes this
+            measures the host; large problems measure the GPU."""
+            comm = torch.cuda.Stream()
+            compute = comm if same_stream else torch.cuda.Stream()
 
-        def go():
-            comm.wait_stream(stream)
-            compute.wait_stream(stream)
-            B.run_overlapped(parts, comm, compute)
-            stream.wait_stream(comm)
-            stream.wait_stream(compute)
+            def go():
+                comm.wait_stream(stream)
+                compute.wait_stream(stream)
+                B.run_overlapped(parts, comm, compute)
+                stream.wait_stream(comm)
+                stream.wait_stream(compute)
 
-        for _ in range(args.warmup):
-            go()
-        return timed(go, args.steps)
+            for _ in range(args.warmup):
+                go()
+            return timed(go, args.steps)
 
-    mb_two, mb_one = micro_batches_ms(False), micro_batches_ms(True)
-    micro = {"parts": 2, "eager": True, "ms_two_streams": round(mb_two, 5), "ms_one_stream": round(mb_one, 5),
-             "tokens_per_s_two_streams": round(w.tokens / (mb_two * 1e-3), 1)}
-    del parts
-    step()   # leave the buffers as the measured form wrote them
+        mb_two, mb_one = micro_batches_ms(False), micro_batches_ms(True)
+        micro = {"parts": 2, "eager": True, "ms_two_streams": round(mb_two, 5), "ms_one_stream": round(mb_one, 5),
+                 "tokens_per_s_two_streams": round(w.tokens / (mb_two * 1e-3), 1)}
+        del parts
+        step()   # leave the buffers as the measured form wrote them
 
     kb = kernel_bytes(w)
     per_kernel = {}
@@ -457,14 +465,14 @@ def main():
             "algorithmic_bytes": dc_bytes, "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
-        "other_mode": {
+        "other_mode": None if not extras else {
             "mode": "base" if direct else "direct",
             "ms_per_step": round(other_ms, 5), "tokens_per_s": round(T / (other_ms * 1e-3), 1),
             "dispatch_combine_ms": round(other_dc_ms, 5),
             "dispatch_combine_tokens_per_s": round(T / (other_dc_ms * 1e-3), 1),
             "dispatch_combine_gbps": round(other_dc_bytes / (other_dc_ms * 1e-3) / 1e9, 1),
         },
-        "allgather_dispatch": {
+        "allgather_dispatch": None if not extras else {
             "dispatch_combine_ms": round(ag_dc_ms, 5), "dispatch_combine_tokens_per_s": round(T / (ag_dc_ms * 1e-3), 1),
             "algorithmic_bytes": sum(kb[n] for n in kt_ag if PHASE_OF[n] in ("dispatch", "combine")),
             "kernels_ms": {n: round(v[1] / v[0], 5) for n, v in kt_ag.items()},
