@@ -237,68 +237,79 @@ __global__ __launch_bounds__(512) void allgather_kernel(const uint4* __restrict_
     }
 }
 
+// Exclusive prefix sum over the experts of the low halves of the histogram
+// entries (two 16-bit counts side by side, each summing to at most N_a <= 8192,
+// so no carry crosses between them) into prefix[0..E], prefix[E] the total.
+// Run by one whole wave: E / 64 entries per lane, then a DPP scan across lanes;
+// the other waves wait at the next block barrier.
+__device__ __forceinline__ void wave_prefix_low(const uint64_t* __restrict__ hist, int32_t* __restrict__ prefix, int E) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per = (E + kWave - 1) / kWave;
+    const int b = lane * per;
+    int run = 0;
+    for (int i = 0; i < per; ++i)
+        if (b + i < E) run += (int)(uint32_t)hist[b + i];
+    const int incl = wave_inclusive_scan(run);
+    int ex = incl - run;
+    for (int i = 0; i < per; ++i)
+        if (b + i < E) {
+            prefix[b + i] = ex;
+            ex += (int)(uint32_t)hist[b + i];
+        }
+    if (lane == kWave - 1) prefix[E] = incl;
+    // the wave's lanes read each other's entries next: LDS accesses of one wave run in order
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+}
+
 // Counts and offsets of source rank s for the handle (one workgroup of the
-// counting form per rank): LDS histograms of all ids, of the ids of ranks
-// below s and of rank s's ids, then one exclusive scan over the experts of
-// both the all-ranks and the rank-s counts (16 bits each: N_a <= 8192).
+// counting form per rank): one LDS histogram entry per expert holding three
+// 16-bit counts (all ids, rank s's ids, the ids of ranks below s), then one
+// wave's prefix sum of the all-ranks and rank-s counts together.
+template <int MI>
 __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int E, int Ep, int k, int P, int Na,
                             int32_t* __restrict__ n, int32_t* __restrict__ N, int32_t* __restrict__ C,
                             int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_recv_off,
                             int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off) {
-    extern __shared__ __align__(16) int32_t hist[];   // [4][E]: all ranks, ranks < s, rank s, rank s's scan
-    __shared__ int32_t tmp[17];
-    int32_t* h_all = hist;
-    int32_t* h_lo = hist + E;
-    int32_t* h_s = hist + 2 * E;
-    int32_t* x_s = hist + 3 * E;
+    extern __shared__ __align__(16) int32_t lds[];   // E 64-bit entries, then E + 1 prefix sums
+    uint64_t* hist = reinterpret_cast<uint64_t*>(lds);
+    int32_t* x_s = lds + 2 * E;
     const int tid = threadIdx.x, bs = blockDim.x;
     const int lo = s * Tp * k, hi = lo + Tp * k;   // rank s's assignments
-    int id[kMaxIdsPerThread];                    // all loads in flight at once (Na <= kMaxIdsPerThread * bs)
-#pragma unroll
-    for (int m = 0; m < kMaxIdsPerThread; ++m) {
-        const int a = tid + m * bs;
-        id[m] = a < Na ? ids[a] : -1;
-    }
-    for (int x = tid; x < 3 * E; x += bs) hist[x] = 0;
+    int id[MI];                                  // all loads in flight at once (Na <= MI * bs; clamped
+#pragma unroll                                   // addresses keep the code straight-line, with no wait per load)
+    for (int m = 0; m < MI; ++m) id[m] = ids[min(tid + m * bs, Na - 1)];
+    for (int x = tid; x < E; x += bs) hist[x] = 0;
     lds_barrier();
 #pragma unroll
-    for (int m = 0; m < kMaxIdsPerThread; ++m) {
+    for (int m = 0; m < MI; ++m) {
         const int a = tid + m * bs;
         const int e = id[m];
-        if ((unsigned)e >= (unsigned)E) continue;   // padding; out-of-range ids are outside the contract, never indexed
-        atomicAdd(&h_all[e], 1);
-        if (a < lo) atomicAdd(&h_lo[e], 1);
-        else if (a < hi) atomicAdd(&h_s[e], 1);
+        if (a >= Na || (unsigned)e >= (unsigned)E) continue;   // out-of-range ids are outside the contract: never indexed
+        const uint64_t inc = 1ull | (a >= lo && a < hi ? 1ull << 16 : 0ull) | (a < lo ? 1ull << 32 : 0ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[e]), (unsigned long long)inc);
     }
     lds_barrier();
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += bs) {          // uniform loop: every thread calls the scan
-        const int e = e0 + tid;
-        const int cs = e < E ? h_s[e] : 0;
-        const int v = e < E ? h_all[e] + (cs << 16) : 0;
-        int tot;
-        const int x = carry + block_exclusive_scan(v, tmp, &tot);
-        if (e < E) {
-            const int eo = x & 0xFFFF, xs = x >> 16;
-            x_s[e] = xs;
-            n[(size_t)s * E + e] = cs;
-            send_off[(size_t)s * E + e] = lo + xs;
-            recv_off[(size_t)s * E + e] = eo + h_lo[e];
-            if (s == 0) {
-                N[e] = h_all[e];
-                expert_off[e] = eo;
-                if (e % Ep == 0) rank_recv_off[e / Ep] = eo;
-            }
+    if (tid < kWave) wave_prefix_low(hist, x_s, E);
+    lds_barrier();
+    for (int e = tid; e < E; e += bs) {
+        const uint64_t h = hist[e];
+        const int all = (int)(h & 0xFFFF), cs = (int)((h >> 16) & 0xFFFF), below = (int)((h >> 32) & 0xFFFF);
+        const int x = x_s[e];
+        const int eo = x & 0xFFFF, xs = x >> 16;
+        n[(size_t)s * E + e] = cs;
+        send_off[(size_t)s * E + e] = lo + xs;
+        recv_off[(size_t)s * E + e] = eo + below;
+        if (s == 0) {
+            N[e] = all;
+            expert_off[e] = eo;
+            if (e % Ep == 0) rank_recv_off[e / Ep] = eo;
         }
-        carry += tot;
     }
-    lds_barrier();
     // C[s][r]: rank s's assignments to rank r's experts, from the scan
-    for (int r = tid; r < P; r += bs)
-        C[(size_t)s * P + r] = (r + 1 < P ? x_s[(r + 1) * Ep] : (carry >> 16)) - x_s[r * Ep];
+    for (int r = tid; r < P; r += bs) C[(size_t)s * P + r] = (x_s[(r + 1) * Ep] >> 16) - (x_s[r * Ep] >> 16);
     if (s == 0 && tid == 0) {
-        expert_off[E] = carry & 0xFFFF;
-        rank_recv_off[P] = carry & 0xFFFF;
+        expert_off[E] = x_s[E] & 0xFFFF;
+        rank_recv_off[P] = x_s[E] & 0xFFFF;
     }
 }
 
@@ -312,8 +323,11 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
 //   recv_pos = #{a : id_a < e} + #{a < t0*k : id_a = e} + c
 //   send_pos = s*(T/P)*k + #{a on rank s : id_a < e} + #{a on rank s, a < t0*k : id_a = e} + c
 // with c = #{t0*k <= a < t*k : id_a = e} (earlier tokens of the same block).
-// Four LDS histograms of the ids (all, before t0, rank s, rank s before t0)
-// and one prefix sum give the first two terms of both.
+// One LDS histogram entry per expert holds four 16-bit counts of the ids (all,
+// rank s's, those before t0, rank s's before t0), so each id costs one 64-bit
+// LDS atomic; one wave's prefix sum over the experts then gives the first term
+// of both positions, and that wave's lanes own the slots.  Three block barriers
+// in all: after clearing the histogram, after the atomics, after the positions.
 template <bool FP8, bool DIRECT, int MI, int TPB, bool ROWS = true>
 __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
                                                          const float* __restrict__ w, uint4* __restrict__ dst,
@@ -329,13 +343,13 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
                                                          int T, int Tp, int E, int Ep, int k, int P, int L) {
     __shared__ int32_t pos[32];
     __shared__ int32_t blk[32];                // the block's own expert ids
-    __shared__ int32_t tmp[17];
     const int slice = blockIdx.y;
     const int tid = threadIdx.x, bs = blockDim.x;
     const int Na = T * k;
     if ((int)blockIdx.x < P) {
         if (slice == 0)
-            rank_counts(ids, blockIdx.x, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off, recv_off);
+            rank_counts<MI>(ids, blockIdx.x, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off,
+                            recv_off);
         return;
     }
     const int t0 = ((int)blockIdx.x - P) * TPB;
@@ -364,13 +378,10 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    extern __shared__ __align__(16) int32_t hist[];   // [5][E]: all, before t0, rank s, rank s before t0, prefix
-    int32_t* h_all = hist;
-    int32_t* h_before = hist + E;
-    int32_t* h_rank = hist + 2 * E;
-    int32_t* h_rank_before = hist + 3 * E;
-    int32_t* prefix = hist + 4 * E;            // exclusive prefix of h_all (low 16 bits) and h_rank (high 16 bits)
-    for (int x = tid; x < 4 * E; x += bs) hist[x] = 0;
+    extern __shared__ __align__(16) int32_t lds[];   // E 64-bit entries, then E + 1 prefix sums
+    uint64_t* hist = reinterpret_cast<uint64_t*>(lds);
+    int32_t* prefix = lds + 2 * E;             // exclusive prefix of (all | rank s << 16)
+    for (int x = tid; x < E; x += bs) hist[x] = 0;
     if (tid < nslots) blk[tid] = my_e;
     lds_barrier();
 #pragma unroll
@@ -378,37 +389,28 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
         const int a = tid + m * bs;
         const int e = raw[m];
         if (a < Na && (unsigned)e < (unsigned)E) {   // out-of-range ids are outside the contract: never indexed
-            atomicAdd(&h_all[e], 1);
-            if (a < t0k) atomicAdd(&h_before[e], 1);
-            if (a >= lo && a < hi) {
-                atomicAdd(&h_rank[e], 1);
-                if (a < t0k) atomicAdd(&h_rank_before[e], 1);
-            }
+            const bool rank = a >= lo && a < hi, before = a < t0k;
+            const uint64_t inc = 1ull | (rank ? 1ull << 16 : 0ull) | (before ? 1ull << 32 : 0ull) |
+                                 (rank && before ? 1ull << 48 : 0ull);
+            atomicAdd(reinterpret_cast<unsigned long long*>(&hist[e]), (unsigned long long)inc);
         }
     }
     lds_barrier();
-    // both prefix sums in one scan (each count is below N_a <= 8192, so 16 bits each)
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += bs) {       // uniform loop: every thread calls the scan
-        const int e = e0 + tid;
-        const int v = e < E ? h_all[e] + (h_rank[e] << 16) : 0;
-        int tot;
-        const int ex = block_exclusive_scan(v, tmp, &tot);
-        if (e < E) prefix[e] = carry + ex;
-        carry += tot;
-    }
-    lds_barrier();
     int p = 0, q = 0;
-    if (tid < nslots) {
-        const int e = min(max(my_e, 0), E - 1);   // in range for any input (out-of-range ids are outside the contract)
-        int c = 0;                              // earlier tokens of this block with the same expert
-        for (int b = 0; b < tid - tid % k; ++b) c += blk[b] == my_e ? 1 : 0;
-        const int pe = prefix[e];
-        q = (pe & 0xFFFF) + h_before[e] + c;
-        p = lo + (pe >> 16) + h_rank_before[e] + c;
-        q = min(q, Na - 1);                     // no-ops for valid input; keep every write in bounds
-        p = min(p, hi - 1);
-        pos[tid] = DIRECT ? q : p;
+    if (tid < kWave) {                         // wave 0: the prefix sum, then the slots (nslots <= 32)
+        wave_prefix_low(hist, prefix, E);
+        if (tid < nslots) {
+            const int e = min(max(my_e, 0), E - 1);   // in range for any input (out-of-range ids are outside the contract)
+            int c = 0;                          // earlier tokens of this block with the same expert
+            for (int b = 0; b < tid - tid % k; ++b) c += blk[b] == my_e ? 1 : 0;
+            const int pe = prefix[e];
+            const uint64_t h = hist[e];
+            q = (pe & 0xFFFF) + (int)((h >> 32) & 0xFFFF) + c;
+            p = lo + (pe >> 16) + (int)(h >> 48) + c;
+            q = min(q, Na - 1);                 // no-ops for valid input; keep every write in bounds
+            p = min(p, hi - 1);
+            pos[tid] = DIRECT ? q : p;
+        }
     }
     lds_barrier();
 #pragma unroll
@@ -422,6 +424,9 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
 }
 
 }  // namespace
+
+// Dynamic LDS of the counting form: E 64-bit histogram entries and E + 1 prefix sums.
+static size_t count_pack_lds(int E) { return sizeof(uint64_t) * (size_t)E + sizeof(int32_t) * ((size_t)E + 1); }
 
 // Ids each thread of the counting form loads (unrolled, all in flight): 4, 8 or 16.
 int ids_per_thread(long long Na, int B) {
@@ -476,7 +481,7 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         using T_ = std::true_type;
         using F_ = std::false_type;
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
-        const size_t lds = 4 * 5 * (size_t)d.E;   // the counting blocks use 3 E, the packing blocks 5 E ints
+        const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
         launch_kernel(kernel, dim3(blocks, (unsigned)slices), dim3(B), lds, st,
                       reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
@@ -516,7 +521,7 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
         };
         auto kernel = mi == 4 ? pick(std::integral_constant<int, 4>{})
                     : mi == 8 ? pick(std::integral_constant<int, 8>{}) : pick(std::integral_constant<int, 16>{});
-        const size_t lds = 4 * 5 * (size_t)d.E;
+        const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
         launch_kernel(kernel, dim3(blocks, 1u), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
                       static_cast<uint4*>(nullptr), static_cast<float*>(nullptr), meta, ws.send_to_recv,
