@@ -240,23 +240,26 @@ __global__ __launch_bounds__(512) void allgather_kernel(const uint4* __restrict_
 // Exclusive prefix sum over the experts of the low halves of the histogram
 // entries (two 16-bit counts side by side, each summing to at most N_a <= 8192,
 // so no carry crosses between them) into prefix[0..E], prefix[E] the total.
-// Run by one whole wave: E / 64 entries per lane, then a DPP scan across lanes;
-// the other waves wait at the next block barrier.
+// Run by one whole wave, 64 experts a row (lane l holds expert 64 i + l of row
+// i): a DPP scan per row, the running total carried from row to row, and the
+// next row's read issued before the current row's scan.  The other waves wait
+// at the next block barrier.
 __device__ __forceinline__ void wave_prefix_low(const uint64_t* __restrict__ hist, int32_t* __restrict__ prefix, int E) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int per = (E + kWave - 1) / kWave;
-    const int b = lane * per;
-    int run = 0;
-    for (int i = 0; i < per; ++i)
-        if (b + i < E) run += (int)(uint32_t)hist[b + i];
-    const int incl = wave_inclusive_scan(run);
-    int ex = incl - run;
-    for (int i = 0; i < per; ++i)
-        if (b + i < E) {
-            prefix[b + i] = ex;
-            ex += (int)(uint32_t)hist[b + i];
-        }
-    if (lane == kWave - 1) prefix[E] = incl;
+    const uint32_t* low = reinterpret_cast<const uint32_t*>(hist);   // low half of entry e at 2 e
+    const int rows = (E + kWave - 1) / kWave;
+    auto row_value = [&](int e) { return e < E ? (int)low[2 * min(e, E - 1)] : 0; };   // clamped, unconditional
+    int next = row_value(lane);
+    int carry = 0;
+    for (int i = 0; i < rows; ++i) {
+        const int v = next;
+        const int e = i * kWave + lane;
+        next = row_value(e + kWave);
+        const int incl = wave_inclusive_scan(v);
+        if (e < E) prefix[e] = carry + incl - v;
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    if (lane == 0) prefix[E] = carry;
     // the wave's lanes read each other's entries next: LDS accesses of one wave run in order
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
 }
