@@ -139,14 +139,16 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Rank whose receive region holds receive row q: the number of region starts
-// rank_recv_off[0..P] that are <= q, less one (a ballot per 64 ranks).
+// rank_recv_off[0..P] that are <= q, less one (a ballot per 64 ranks; the
+// loads use clamped addresses, so loads the caller issued before stay in
+// flight with them).
 __device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_off, int P, int q) {
     const int lane = threadIdx.x & (kWave - 1);
     int count = 0;
     for (int r0 = 0; r0 <= P; r0 += kWave) {
         const int r = r0 + lane;
-        const bool le = r <= P && rank_recv_off[r] <= q;
-        count += __popcll(__ballot(le));
+        const int start = rank_recv_off[min(r, P)];
+        count += __popcll(__ballot(r <= P && start <= q));
     }
     return count - 1;
 }

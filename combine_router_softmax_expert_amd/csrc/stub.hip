@@ -28,15 +28,19 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
     const int q = blockIdx.x;
     const int slice = blockIdx.y;
     const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
-    uint4 c = make_uint4(0u, 0u, 0u, 0u);
-    if (u < L) c = ld16<NTL>(&recv[(size_t)q * L + u]);   // issued first: overlaps the expert lookup
+    // every load first, unconditional at clamped addresses, so that all of them
+    // are in flight before the first wait: one memory round trip in all
+    const int uc = min(u, L - 1);
+    const uint4 c = ld16<NTL>(&recv[(size_t)q * L + uc]);
+    float sc = 0.0f;
+    if constexpr (FP8) sc = scales[(size_t)q * (L / 8) + (uc >> 3)];
+    const int local = meta[q].local_expert;
     __builtin_amdgcn_sched_barrier(0);
     const int r = owner_rank(rank_recv_off, P, q);
-    const int e = r * Ep + meta[q].local_expert;
+    const int e = r * Ep + local;
     const float m = (float)(E + e) / (float)E;
     if (u >= L) return;
     if (FP8) {
-        const float sc = scales[(size_t)q * (L / 8) + (u >> 3)];
         float f[16];
         unpack4_e4m3(c.x, f);
         unpack4_e4m3(c.y, f + 4);
