@@ -315,6 +315,22 @@ def main():
     # dispatch + combine alone, K times back to back
     dc_ms = timed(dispatch_combine, args.steps)
 
+    def latency_percentiles(fn, n):
+        """Median, p95 and p99 of n back-to-back calls, each bracketed by its own events."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        return {"median": round(float(np.median(t)), 5), "p95": round(float(np.percentile(t, 95)), 5),
+                "p99": round(float(np.percentile(t, 99)), 5)}
+
+    latency_ms = {"step": latency_percentiles(step, args.steps),
+                  "dispatch_combine": latency_percentiles(dispatch_combine, args.steps)}
+
     # the same K steps with every kernel bracketed by HIP events on its stream
     # (the library records them around each launch), for per-kernel durations;
     # each event pair adds launch-to-launch overhead, so these read high for
@@ -481,6 +497,7 @@ def main():
         "micro_batches": micro,
         "phases_ms": {k: round(v, 5) for k, v in phases.items()},
         "kernels": per_kernel,
+        "latency_ms": latency_ms,
         "ms_per_step_with_kernel_events": round(ms_with_events, 5),
         "ms_per_step_cache_flushed": None if cold_ms is None else round(cold_ms, 5),
         "metadata_bytes_per_step": metadata_bytes(w),
