@@ -207,7 +207,10 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
     const long long Na = T * s.top_k;
     if (s.num_experts > 1024 || s.num_experts / s.num_ranks > 32767 || s.top_k > 32 || s.hidden > 65536 ||
         (fp8 && s.hidden % kFp8Block != 0) || Na >= (1LL << 31) ||
-        Na * (s.hidden / 1024 + 1) >= (1LL << 31))
+        Na * (s.hidden / 1024 + 1) >= (1LL << 31) ||
+        // a row kernel's grid is at most N_a + P rows of H/8 units rounded up to a
+        // workgroup (< 512 more), in one dimension of fewer than 2^32 work-items
+        (Na + s.num_ranks) * (s.hidden / 8 + 512) >= (1LL << 32))
         return MOE_ERR_UNSUPPORTED;
 
     moe_ctx* ctx = new (std::nothrow) moe_ctx();
@@ -394,7 +397,8 @@ moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t
     if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf)) return MOE_ERR_INVALID_ARG;
     if (d.fp8 ? (d.T > 0 && (!gathered_scales || !recv_scales)) : (gathered_scales || recv_scales))
         return MOE_ERR_INVALID_ARG;
-    if ((long long)d.P * d.T >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;   // gathered rows are indexed in 32 bits
+    // the gathered rows (P * T of them, indexed in 32 bits) in one grid dimension of fewer than 2^32 work-items
+    if ((long long)d.P * d.T * (d.H / 8 + 512) >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -153,6 +153,18 @@ __device__ __forceinline__ int owner_rank(const int32_t* __restrict__ rank_recv_
     return count - 1;
 }
 
+// Row and slice of this workgroup in a 1-D grid of rows x slices workgroups
+// with the slices of a row adjacent (row_grid on the host).
+struct RowSlice {
+    int row, slice;
+};
+__device__ __forceinline__ RowSlice row_slice(int slices) {
+    const int b = blockIdx.x;
+    // one and two slices (rows up to 8 KiB, and up to 16 KiB) skip the integer division
+    const int row = slices == 1 ? b : slices == 2 ? b >> 1 : b / slices;
+    return {row, b - row * slices};
+}
+
 // Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
 // `tmp` needs blockDim.x / 64 + 1 ints of LDS.  Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {

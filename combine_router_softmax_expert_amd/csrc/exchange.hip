@@ -29,9 +29,8 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
                                                        const float* __restrict__ send_scales,
                                                        float* __restrict__ recv_scales,
                                                        const uint4* __restrict__ send_meta,
-                                                       uint4* __restrict__ recv_meta, int L, int nb) {
-    const int b = blockIdx.x;
-    const int slice = blockIdx.y;
+                                                       uint4* __restrict__ recv_meta, int L, int nb, int slices) {
+    const auto [b, slice] = row_slice(slices);
     const int u = slice * blockDim.x + threadIdx.x;
     int p, q;
     uint4 v;
@@ -55,9 +54,8 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
 __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uint4* __restrict__ expert_out,
                                                                        uint4* __restrict__ comb,
                                                                        const HandleRecord* __restrict__ recv_meta, int Tp,
-                                                                       int k, int L) {
-    const int q = blockIdx.x;
-    const int slice = blockIdx.y;
+                                                                       int k, int L, int slices) {
+    const auto [q, slice] = row_slice(slices);
     const int u = slice * blockDim.x + threadIdx.x;
     uint4 v;
     if (u < L) v = expert_out[(size_t)q * L + u];   // data first: its load overlaps the record's
@@ -69,9 +67,9 @@ __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uin
 
 __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint4* __restrict__ expert_out,
                                                                       uint4* __restrict__ comb,
-                                                                      const int32_t* __restrict__ recv_pos, int L) {
-    const int c = blockIdx.x;                   // combine row t*k + j
-    const int slice = blockIdx.y;
+                                                                      const int32_t* __restrict__ recv_pos, int L,
+                                                                      int slices) {
+    const auto [c, slice] = row_slice(slices);  // combine row t*k + j
     const int q = recv_pos[c];
     const int u = slice * blockDim.x + threadIdx.x;
     if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
@@ -88,14 +86,14 @@ __global__ __launch_bounds__(512) void select_kernel(const uint4* __restrict__ g
                                                      uint4* __restrict__ recv, float* __restrict__ recv_scales,
                                                      const HandleRecord* __restrict__ recv_meta,
                                                      const int32_t* __restrict__ rank_recv_off, int P, int T, int Tp,
-                                                     int L, int nb) {
-    const int q = blockIdx.x;
-    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+                                                     int L, int nb, int slices) {
+    const auto [q, slice] = row_slice(slices);
+    const int u = slice * blockDim.x + threadIdx.x;
     const int r = owner_rank(rank_recv_off, P, q);
     const HandleRecord m = recv_meta[q];
     const size_t src = (size_t)r * T + (size_t)m.src_rank * Tp + m.src_token;
     if (u < L) st16<NT>(&recv[(size_t)q * L + u], ld16<NT>(&gathered[src * L + u]));
-    if (blockIdx.y == 0)
+    if (slice == 0)
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = gathered_scales[src * nb + x];
 }
 
@@ -109,10 +107,10 @@ __global__ __launch_bounds__(512) void select_scatter_kernel(const uint4* __rest
                                                              uint4* __restrict__ recv, float* __restrict__ recv_scales,
                                                              const int32_t* __restrict__ ids,
                                                              const int32_t* __restrict__ recv_pos, int T, int Ep, int k,
-                                                             int L, int nb) {
-    const int g = blockIdx.x;                  // row r*T + t of the gathered copies
+                                                             int L, int nb, int slices) {
+    const auto [g, slice] = row_slice(slices);   // row r*T + t of the gathered copies
     const int r = g / T, t = g - r * T;
-    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+    const int u = slice * blockDim.x + threadIdx.x;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (u < L) v = ld16<NT>(&gathered[(size_t)g * L + u]);
     for (int j = 0; j < k; ++j) {
@@ -120,7 +118,7 @@ __global__ __launch_bounds__(512) void select_scatter_kernel(const uint4* __rest
         if (ids[a] / Ep != r) continue;        // uniform: the same slot in every lane
         const int q = recv_pos[a];
         if (u < L) st16<NT>(&recv[(size_t)q * L + u], v);
-        if (blockIdx.y == 0)
+        if (slice == 0)
             for (int x = threadIdx.x; x < nb; x += blockDim.x)
                 recv_scales[(size_t)q * nb + x] = gathered_scales[(size_t)g * nb + x];
     }
@@ -137,15 +135,16 @@ hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids,
     const bool nt = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     if (d.P <= 2 * d.k) {
         auto kernel = nt ? select_scatter_kernel<true> : select_scatter_kernel<false>;
-        launch_kernel(kernel, dim3((unsigned)(d.P * d.T), (unsigned)slices), dim3(B), 0, st,
+        launch_kernel(kernel, row_grid((long long)d.P * d.T, slices), dim3(B), 0, st,
                       reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv),
-                      recv_scales, ids, ws.recv_pos, d.T, d.Ep, d.k, L, d.scales);
+                      recv_scales, ids, ws.recv_pos, d.T, d.Ep, d.k, L, d.scales, slices);
         return hipGetLastError();
     }
     auto kernel = nt ? select_kernel<true> : select_kernel<false>;
-    launch_kernel(kernel, dim3((unsigned)d.Na, (unsigned)slices), dim3(B), 0, st,
+    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                   reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv), recv_scales,
-                  reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, d.P, d.T, d.Tp, L, d.scales);
+                  reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, d.P, d.T, d.Tp, L, d.scales,
+                  slices);
     return hipGetLastError();
 }
 
@@ -157,11 +156,11 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int slices = (L + B - 1) / B;
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
-    launch_kernel(kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
-                       gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
-                       reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L,
-                       d.scales);
+    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+                  reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
+                  gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
+                  reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales,
+                  slices);
     return hipGetLastError();
 }
 
@@ -172,12 +171,12 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (streaming(d, 2LL * d.Na * 16LL * L))
-        launch_kernel(reverse_exchange_gather_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
-                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L);
+        launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L, slices);
     else
-        launch_kernel(reverse_exchange_scatter_kernel, dim3((unsigned)(d.Na), (unsigned)slices), dim3(B), 0, st,
-                           reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                           reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L);
+        launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
+                      reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
     return hipGetLastError();
 }
 

@@ -104,6 +104,13 @@ inline bool streaming(const Dims& d, long long bytes) {
 
 // Threads per block for a row of `n` per-thread work items: the whole row when it
 // fits in 512 threads, else a divisor of n from 512 down to 256, else 256.
+// Grid of a row kernel: rows x slices workgroups in one dimension, the slices of
+// a row adjacent, so that workgroups issued together cover consecutive bytes
+// (measured on gfx950 with 14 KiB rows: a gathering copy 5.6 -> 6.0 TB/s and
+// the weighted reduction 5.7 -> 5.9 TB/s against a (rows, slices) grid).  The
+// shape limits keep rows x slices x block below 2^32 work-items.
+inline dim3 row_grid(long long rows, int slices) { return dim3((unsigned)(rows * slices)); }
+
 inline int pick_block(long long n) {
     if (n <= 512) return (int)((n + 63) / 64 * 64);
     for (int b = 512; b >= 256; b -= 64)

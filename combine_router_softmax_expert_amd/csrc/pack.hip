@@ -165,10 +165,9 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
                                                    HandleRecord* __restrict__ dst_meta, int32_t* __restrict__ send_to_recv,
                                                    int32_t* __restrict__ recv_to_send,
                                                    int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
-                                                   int Tp, int E, int Ep, int k, int L) {
+                                                   int Tp, int E, int Ep, int k, int L, int slices) {
     __shared__ int32_t pos[32];
-    const int t = blockIdx.x;
-    const int slice = blockIdx.y;
+    const auto [t, slice] = row_slice(slices);
     const int s = t / Tp;
     const int tid = threadIdx.x;
     const int u = slice * blockDim.x + tid;   // 16-byte output unit of the row
@@ -222,10 +221,11 @@ __global__ __launch_bounds__(256) void handle_kernel(const int32_t* __restrict__
 // scales computed once), lands in row r*T + t of every rank r's copy.
 template <bool FP8, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void allgather_kernel(const uint4* __restrict__ x, uint4* __restrict__ gathered,
-                                                        float* __restrict__ gathered_scales, int T, int P, int L) {
+                                                        float* __restrict__ gathered_scales, int T, int P, int L,
+                                                        int slices) {
     __shared__ int32_t pos[kMaxRanksPerStore];
-    const int t = blockIdx.x;
-    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+    const auto [t, slice] = row_slice(slices);
+    const int u = slice * blockDim.x + threadIdx.x;
     uint4 xa, xb;
     load_row<FP8, NTL>(x, t, L, u, xa, xb);
     for (int r0 = 0; r0 < P; r0 += kMaxRanksPerStore) {   // copies in groups of the position table
@@ -316,8 +316,8 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
     }
 }
 
-// Grid (P + ceil(T / TPB), slices): block s < P of slice 0 writes rank s's
-// counts and offsets (the other slices of those blocks exit); block P + b packs
+// Grid of P + ceil(T / TPB) rows of slices (row_grid): row s < P, slice 0,
+// writes rank s's counts and offsets (the other slices of those rows exit); row P + b packs
 // tokens b*TPB .. b*TPB + TPB - 1 (all on one rank: TPB divides T/P), whose
 // TPB * k <= 32 assignments ("slots") share one counting pass.  The counting
 // blocks come first so they run alongside the packing ones.
@@ -343,19 +343,19 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
                                                          int32_t* __restrict__ C, int32_t* __restrict__ expert_off,
                                                          int32_t* __restrict__ rank_recv_off,
                                                          int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off,
-                                                         int T, int Tp, int E, int Ep, int k, int P, int L) {
+                                                         int T, int Tp, int E, int Ep, int k, int P, int L,
+                                                         int slices) {
     __shared__ int32_t pos[32];
     __shared__ int32_t blk[32];                // the block's own expert ids
-    const int slice = blockIdx.y;
+    const auto [b, slice] = row_slice(slices);
     const int tid = threadIdx.x, bs = blockDim.x;
     const int Na = T * k;
-    if ((int)blockIdx.x < P) {
+    if (b < P) {
         if (slice == 0)
-            rank_counts<MI>(ids, blockIdx.x, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off,
-                            recv_off);
+            rank_counts<MI>(ids, b, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off, recv_off);
         return;
     }
-    const int t0 = ((int)blockIdx.x - P) * TPB;
+    const int t0 = (b - P) * TPB;
     const int ntok = min(TPB, T - t0);
     const int nslots = ntok * k;               // <= 32 by the launch condition
     const int s = t0 / Tp;                     // the block's rank
@@ -486,11 +486,11 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
-        launch_kernel(kernel, dim3(blocks, (unsigned)slices), dim3(B), lds, st,
+        launch_kernel(kernel, row_grid(blocks, slices), dim3(B), lds, st,
                       reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
                       ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
                       ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
-                      L);
+                      L, slices);
         return hipGetLastError();
     }
     const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));
@@ -502,10 +502,10 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         if (direct) kernel = nt ? pack_kernel<false, true, false, true> : pack_kernel<false, false, false, true>;
         else kernel = nt ? pack_kernel<false, true, false, false> : pack_kernel<false, false, false, false>;
     }
-    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
-                       reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
-                       ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L);
+    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st,
+                  reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
+                  reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
+                  ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L, slices);
     return hipGetLastError();
 }
 
@@ -526,10 +526,10 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
                     : mi == 8 ? pick(std::integral_constant<int, 8>{}) : pick(std::integral_constant<int, 16>{});
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
-        launch_kernel(kernel, dim3(blocks, 1u), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
+        launch_kernel(kernel, row_grid(blocks, 1), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
                       static_cast<uint4*>(nullptr), static_cast<float*>(nullptr), meta, ws.send_to_recv,
                       ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C, ws.expert_off, ws.rank_recv_off,
-                      ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P, d.row_units);
+                      ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P, d.row_units, 1);
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)((d.Na + 255) / 256);
@@ -546,8 +546,8 @@ hipError_t launch_allgather(const Dims& d, const uint16_t* x, void* gathered, fl
     const bool nt = streaming(d, 2LL * d.H * d.T + (long long)d.P * d.T * (16LL * L + 4LL * d.scales));
     auto kernel = d.fp8 ? (nt ? allgather_kernel<true, true, false> : allgather_kernel<true, false, false>)
                         : (nt ? allgather_kernel<false, true, false> : allgather_kernel<false, false, false>);
-    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x),
-                  reinterpret_cast<uint4*>(gathered), gathered_scales, d.T, d.P, L);
+    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x),
+                  reinterpret_cast<uint4*>(gathered), gathered_scales, d.T, d.P, L, slices);
     return hipGetLastError();
 }
 

@@ -22,9 +22,10 @@ constexpr int kChunk = 8;
 
 template <bool NTL, bool NTS, bool DIRECT>
 __global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
-                                                     const float* __restrict__ w, uint4* __restrict__ y, int k, int L) {
-    const int t = blockIdx.x;
-    const int u = blockIdx.y * blockDim.x + threadIdx.x;
+                                                     const float* __restrict__ w, uint4* __restrict__ y, int k, int L,
+                                                     int slices) {
+    const auto [t, slice] = row_slice(slices);
+    const int u = slice * blockDim.x + threadIdx.x;
     if (u >= L) return;
     float acc[8];
 #pragma unroll
@@ -64,8 +65,8 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
     const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
     auto kernel = direct ? (nt ? reduce_kernel<true, true, true> : reduce_kernel<false, false, true>)
                          : (nt ? reduce_kernel<true, true, false> : reduce_kernel<false, false, false>);
-    launch_kernel(kernel, dim3((unsigned)d.T, (unsigned)slices), dim3(B), 0, st,
-                       reinterpret_cast<const uint4*>(rows), recv_pos, w, reinterpret_cast<uint4*>(y), d.k, L);
+    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
+                  reinterpret_cast<uint4*>(y), d.k, L, slices);
     return hipGetLastError();
 }
 

@@ -24,9 +24,8 @@ template <bool FP8, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
                                                    const HandleRecord* __restrict__ meta,
                                                    const int32_t* __restrict__ rank_recv_off,
-                                                   uint4* __restrict__ out, int P, int E, int Ep, int L) {
-    const int q = blockIdx.x;
-    const int slice = blockIdx.y;
+                                                   uint4* __restrict__ out, int P, int E, int Ep, int L, int slices) {
+    const auto [q, slice] = row_slice(slices);
     const int u = slice * blockDim.x + threadIdx.x;   // input unit of 16 bytes
     // every load first, unconditional at clamped addresses, so that all of them
     // are in flight before the first wait: one memory round trip in all
@@ -72,14 +71,13 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     const int L = d.row_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    const dim3 grid((unsigned)d.Na, (unsigned)slices);
     const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
     // streaming: e4m3 rows load nontemporally, bf16 rows store nontemporally (best of the four choices each)
     auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, false> : stub_kernel<true, false, false>)
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
-    launch_kernel(kernel, grid, dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
-                       reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
-                       d.P, d.E, d.Ep, L);
+    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+                  reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
+                  d.P, d.E, d.Ep, L, slices);
     return hipGetLastError();
 }
 

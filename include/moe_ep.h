@@ -62,7 +62,8 @@ typedef enum {
 
 /* Problem shape.  Limits: 1 <= P; E % P == 0; E <= 1024; E/P <= 32767;
  * 1 <= k <= min(E, 32); H % 8 == 0 and 8 <= H; FP8 needs H % 128 == 0;
- * T * k < 2^31. */
+ * T * k < 2^31, T * k * (H/1024 + 1) < 2^31 and (T * k + P) * (H/8 + 512) < 2^32
+ * (the grid of a row kernel). */
 typedef struct {
     int32_t num_ranks;
     int32_t tokens_per_rank;
@@ -241,7 +242,7 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
  *   gathered_scales  fp32 [P*T][H/128] out (e4m3 only, else NULL)
  * Other arguments as moe_dispatch.
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_HIP; MOE_ERR_UNSUPPORTED
- * when P * T >= 2^31 (the gathered rows). */
+ * when P * T * (H/8 + 512) >= 2^32 (the gathered rows in one grid dimension). */
 moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                   void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
                                   void* recv_buf, float* recv_scales, moe_handle* handle, void* stream);

@@ -43,7 +43,7 @@ def _create(b, P=4, Tp=16, E=8, k=2, H=256, dt=0):
     (dict(P=0), -1), (dict(Tp=-1), -1), (dict(E=6, P=4), -1), (dict(k=0), -1), (dict(k=9, E=8), -1),
     (dict(H=4), -1), (dict(H=260), -1), (dict(dt=2), -1),
     (dict(E=2048, P=4), -2), (dict(k=33, E=64), -2), (dict(dt=1, H=200), -2), (dict(H=131072), -2),
-    (dict(P=1, Tp=1 << 28, k=8), -2),
+    (dict(P=1, Tp=1 << 28, k=8), -2), (dict(P=1, Tp=8_400_000, k=1, H=8), -2),
 ])
 def test_ctx_create_rejects_bad_shapes(b, args, code):
     st, h = _create(b, **args)
@@ -224,7 +224,7 @@ def test_allgather_dispatch_validates_arguments(b):
     assert A(h, fake, fake, fake, fake, ws - 1, fake, None, fake, None, ctypes.byref(hd), None) == -3
     assert A(h, fake, fake, fake, fake, ws, fake, None, fake, None, None, None) == -1
     b.lib.moe_ctx_destroy(h)
-    st, hbig = _create(b, P=2, Tp=(1 << 30) - 1, E=2, k=1, H=8)     # P * T >= 2^31 gathered rows
+    st, hbig = _create(b, P=2, Tp=2_250_000, E=2, k=1, H=8)     # P * T * (H/8 + 512) >= 2^32 gathered work-items
     assert st == 0
     assert b.lib.moe_dispatch_allgather(hbig, fake, fake, fake, fake, b.lib.moe_workspace_bytes(hbig), fake, None,
                                         fake, None, ctypes.byref(hd), None) == -2
