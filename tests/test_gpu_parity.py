@@ -192,6 +192,8 @@ EDGE = [
     ("two-tokens-per-block", 6, 342, 12, 3, 4096, False),
     ("four-tokens-per-block-fp8", 4, 1024, 8, 2, 8192, True),
     ("E-odd-96", 3, 50, 96, 5, 520, False),
+    ("six-slices-ragged-row", 2, 6, 8, 2, 10248, False),   # 1281 units: 6 workgroups of 256, the last partial
+    ("three-slices-fp8", 2, 5, 8, 2, 24576, True),         # 1536 code units (3 x 512), 3072 output units (6 x 512)
 ]
 
 
