@@ -297,3 +297,100 @@ def test_zero_tokens(orc):
     B.moe_expert_stub(ctx, h, bufs["recv"], None, bufs["expert_out"])
     B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
     torch.cuda.synchronize()
+
+
+def _random_shapes(n, seed):
+    """Seeded random shapes over the ranges of the test plan: P in {1, 2, 3, 4, 8, 32}, E a multiple of P,
+    k <= min(E, 8), H in {8, 128, 136, 7168} (FP8: {128, 7168}), T/P in 1..300, capped so the oracle
+    stays within a second."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        P = int(rng.choice([1, 2, 3, 4, 8, 32]))
+        E = P * int(rng.integers(1, 9))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        fp8 = bool(rng.integers(0, 2))
+        H = int(rng.choice([128, 7168] if fp8 else [8, 128, 136, 7168]))
+        Tp = min(int(rng.integers(1, 301)), max(1, (1 << 20) // (P * H)))
+        mode = ("base", "direct", "allgather")[i % 3]
+        shapes.append((f"rand{i}-P{P}-Tp{Tp}-E{E}-k{k}-H{H}-{'fp8' if fp8 else 'bf16'}-{mode}", P, Tp, E, k, H, fp8,
+                       mode))
+    return shapes
+
+
+RANDOM_SHAPES = _random_shapes(18, 20261202)
+
+
+@pytest.mark.parametrize("name,P,Tp,E,k,H,fp8,mode", RANDOM_SHAPES, ids=[s[0] for s in RANDOM_SHAPES])
+def test_random_shapes(orc, name, P, Tp, E, k, H, fp8, mode):
+    sh = orc.Shape(P, P * Tp, E, k, H, fp8)
+    seed = zlib.crc32(name.encode())
+    x = wl.make_hidden(seed, sh.T, H)
+    logits = wl.make_logits(seed, sh.T, E)
+    _full_parity(orc, sh, x, logits=logits, label=name, direct=mode == "direct", allgather=mode == "allgather")
+
+
+GUARD = 4096   # bytes of 0xA5 on each side of every buffer (keeps the 256-byte workspace alignment)
+
+
+def _guarded(t):
+    """A buffer of t's shape and dtype in the middle of a larger one whose edges hold a known pattern."""
+    import torch
+    if t is None:
+        return None, None
+    n = t.numel() * t.element_size()
+    big = torch.full((n + 2 * GUARD,), 0xA5, dtype=torch.uint8, device=t.device)
+    return big[GUARD:GUARD + n].view(t.dtype).view(t.shape), big
+
+
+@pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", [("guard-bf16", 4, 33, 8, 2, 136, False),
+                                                 ("guard-fp8-ragged", 3, 7, 6, 3, 384, True),
+                                                 ("guard-counting-pack", 8, 16, 64, 8, 1024, False)])
+@pytest.mark.parametrize("mode", ["base", "direct", "allgather"])
+@pytest.mark.parametrize("count", ["auto", "separate"])
+def test_no_writes_outside_buffers(orc, monkeypatch, name, P, Tp, E, k, H, fp8, mode, count):
+    """Every output buffer sits between guard bands; after the whole path the bands are intact and y matches
+    the oracle, so no kernel writes past either end of a caller's buffer."""
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    monkeypatch.setenv("MOE_EP_COUNT_PATH", count)
+    log(f"[guard] {name} {mode} count={count}")
+    ctx = B.Context(P, Tp, E, k, H, fp8)
+    bufs, bigs = {}, {}
+    plain = ctx.allocate()
+    if mode == "allgather":
+        plain["gathered"], plain["gathered_scales"] = ctx.allocate_gathered()
+    for key, t in plain.items():
+        bufs[key], bigs[key] = _guarded(t)
+    sh = orc.Shape(P, P * Tp, E, k, H, fp8)
+    seed = zlib.crc32(name.encode())
+    x_np = wl.make_hidden(seed, sh.T, H)
+    logits_np = wl.make_logits(seed, sh.T, E)
+    x = torch.from_numpy(x_np.view(np.int16)).cuda()
+    logits = torch.from_numpy(logits_np).cuda()
+    B.moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"])
+    if mode == "allgather":
+        h = B.moe_dispatch_allgather(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["gathered"],
+                                     bufs["gathered_scales"], bufs["recv"], bufs["recv_scales"])
+    elif mode == "direct":
+        h = B.moe_dispatch_direct(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
+                                  bufs["recv_scales"])
+    else:
+        h = B.moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
+                           bufs["send_scales"], bufs["recv"], bufs["recv_scales"])
+    B.moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"])
+    if mode == "direct":
+        B.moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"])
+    else:
+        B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
+    torch.cuda.synchronize()
+    for key, big in bigs.items():
+        if big is None:
+            continue
+        edges = torch.cat([big[:GUARD], big[-GUARD:]]).cpu().numpy()
+        assert (edges == 0xA5).all(), (name, mode, key)
+    o_ids, o_w = orc.route(sh, logits_np)
+    assert np.array_equal(bufs["topk_ids"].cpu().numpy(), o_ids)
+    o = orc.run(sh, x_np, ids=o_ids, w=bufs["topk_w"].cpu().numpy())
+    assert np.array_equal(bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16), o["y"].view(np.uint16))
