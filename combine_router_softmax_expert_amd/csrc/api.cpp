@@ -37,6 +37,7 @@ struct moe_ctx {
     uint64_t generation = 0;
     uint64_t received = 0;       // generation whose receive side is complete (exchange or direct pack)
     uint64_t combine_sent = 0;   // generation whose reverse exchange was issued
+    uint64_t direct_sent = 0;    // generation dispatched by moe_dispatch_direct
     void* workspace = nullptr;   // workspace of the latest dispatch (the split receive phase reads its maps)
     bool timing = false;
     bool debug = false;    // MOE_EP_DEBUG: validate ids on the device (and synchronise) before dispatching
@@ -109,6 +110,14 @@ moe::Workspace from_handle(const moe_handle* h) {
     w.recv_pos = const_cast<int32_t*>(h->recv_pos);
     w.recv_meta = const_cast<moe_meta*>(h->recv_meta);
     return w;
+}
+
+// Whether the kernels that work on a handle's rows take the token-affine layout
+// (moe::token_affine): after a direct dispatch, whose pack wrote the receive
+// rows in that layout, or everywhere when MOE_EP_LAYOUT=tokens asks for it.
+bool affine_layout(const moe_ctx* ctx, const moe_handle* h) {
+    if (!moe::token_affine(ctx->d)) return false;
+    return h->generation == ctx->direct_sent || ctx->d.layout == moe::Layout::kTokens;
 }
 
 // Publishes a dispatch: bumps the ctx generation and points the handle at the
@@ -243,6 +252,12 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
         if (std::strcmp(cp, "separate") == 0) d.count_path = moe::CountPath::kSeparate;
         if (std::strcmp(cp, "fused") == 0) d.count_path = moe::CountPath::kFused;
     }
+    // MOE_EP_LAYOUT=rows|tokens overrides the size-based workgroup layout (for A/B tests)
+    d.layout = moe::Layout::kAuto;
+    if (const char* lay = std::getenv("MOE_EP_LAYOUT")) {
+        if (std::strcmp(lay, "rows") == 0) d.layout = moe::Layout::kRows;
+        if (std::strcmp(lay, "tokens") == 0) d.layout = moe::Layout::kTokens;
+    }
 
     const size_t P = d.P, E = d.E, tk = (size_t)Na;
     size_t off = 0;
@@ -336,7 +351,8 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
         const moe::Workspace ws = carve(ctx, ctx->workspace);
         hipStream_t st = static_cast<hipStream_t>(stream);
         s = launch(ctx, "exchange", st, [&] {
-            return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, st);
+            return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, affine_layout(ctx, handle),
+                                        st);
         });
         if (s != MOE_OK) return s;
     }
@@ -384,6 +400,7 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
     ctx->workspace = workspace;
     fill_handle(ctx, ws, handle, false);
     ctx->received = ctx->generation;
+    ctx->direct_sent = ctx->generation;
     return MOE_OK;
 }
 
@@ -433,7 +450,9 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
     if (!recv_buf || !expert_out || (d.fp8 ? !recv_scales : recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
     const moe::Workspace ws = from_handle(handle);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch(ctx, "stub", st, [&] { return moe::launch_stub(d, ws, recv_buf, recv_scales, expert_out, st); });
+    const bool affine = affine_layout(ctx, handle);
+    return launch(ctx, "stub", st,
+                  [&] { return moe::launch_stub(d, ws, recv_buf, recv_scales, expert_out, affine, st); });
 }
 
 moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
@@ -447,7 +466,9 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
         const moe::Workspace ws = from_handle(handle);
         hipStream_t st = static_cast<hipStream_t>(stream);
         s = launch(ctx, "reverse_exchange", st,
-                   [&] { return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, st); });
+                   [&] {
+                       return moe::launch_reverse_exchange(d, ws, expert_out, comb_buf, affine_layout(ctx, handle), st);
+                   });
         if (s != MOE_OK) return s;
     }
     ctx->combine_sent = ctx->generation;
@@ -467,7 +488,9 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
     if (d.T == 0) return MOE_OK;
     if (!comb_buf || !topk_w || !y) return MOE_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch(ctx, "reduce", st, [&] { return moe::launch_reduce(d, comb_buf, nullptr, topk_w, y, false, st); });
+    const bool affine = affine_layout(ctx, handle);
+    return launch(ctx, "reduce", st,
+                  [&] { return moe::launch_reduce(d, comb_buf, nullptr, topk_w, y, false, affine, st); });
 }
 
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out, const float* topk_w,
@@ -491,7 +514,7 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
     if (!expert_out || !topk_w || !y) return MOE_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launch(ctx, "reduce_direct", st, [&] {
-        return moe::launch_reduce(d, expert_out, handle->recv_pos, topk_w, y, true, st);
+        return moe::launch_reduce(d, expert_out, handle->recv_pos, topk_w, y, true, affine_layout(ctx, handle), st);
     });
 }
 

@@ -165,6 +165,21 @@ __device__ __forceinline__ RowSlice row_slice(int slices) {
     return {row, b - row * slices};
 }
 
+// Work item of this workgroup in a token-affine grid (TokenGrid on the host):
+// token t, slot j and slice; false for the workgroups that pad a round to a
+// power of two, and past the last token.
+__device__ __forceinline__ bool token_item(int groups, int slices, int tpb_log2, int m_log2, int T, int& t, int& j,
+                                           int& slice) {
+    const int w = blockIdx.x;
+    const int round = w >> m_log2, rem = w & ((1 << m_log2) - 1);
+    if (rem >= groups * slices) return false;
+    const int g = slices == 1 ? rem : slices == 2 ? rem >> 1 : rem / slices;
+    slice = rem - g * slices;
+    j = round >> tpb_log2;
+    t = (g << tpb_log2) + (round & ((1 << tpb_log2) - 1));
+    return t < T;
+}
+
 // Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64).
 // `tmp` needs blockDim.x / 64 + 1 ints of LDS.  Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {

@@ -75,6 +75,42 @@ __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint
     if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
 }
 
+// Token-affine forms (cache-resident bf16 problems, token_affine): workgroup
+// (t, j, slice) moves the rows of assignment t*k + j on the XCD whose L2 holds
+// what the previous kernel wrote for that token and slice.  The positions come
+// from the handle (every slice of the pack wrote them), then the row.
+__global__ __launch_bounds__(512) void exchange_affine_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
+                                                              const int32_t* __restrict__ send_pos,
+                                                              const int32_t* __restrict__ recv_pos,
+                                                              const float* __restrict__ send_scales,
+                                                              float* __restrict__ recv_scales,
+                                                              const uint4* __restrict__ send_meta,
+                                                              uint4* __restrict__ recv_meta, int L, int nb, int k, int T,
+                                                              TokenGrid tg) {
+    int t, j, slice;
+    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    const int a = t * k + j;
+    const int p = send_pos[a], q = recv_pos[a];
+    const int u = slice * blockDim.x + threadIdx.x;
+    if (u < L) recv[(size_t)q * L + u] = send[(size_t)p * L + u];
+    if (slice == 0) {
+        for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
+        if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
+    }
+}
+
+__global__ __launch_bounds__(512) void reverse_exchange_affine_kernel(const uint4* __restrict__ expert_out,
+                                                                      uint4* __restrict__ comb,
+                                                                      const int32_t* __restrict__ recv_pos, int L, int k,
+                                                                      int T, TokenGrid tg) {
+    int t, j, slice;
+    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    const int a = t * k + j;                    // combine row of the assignment
+    const int q = recv_pos[a];
+    const int u = slice * blockDim.x + threadIdx.x;
+    if (u < L) comb[(size_t)a * L + u] = expert_out[(size_t)q * L + u];
+}
+
 // The all-gather dispatcher's local pick ("Expert Parallel: MoE Token ...",
 // section "为什么不用 AllGather 收集所有 token": each rank picks its own
 // assignments out of the gathered tokens): receive row q of rank r takes the
@@ -149,11 +185,18 @@ hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids,
 }
 
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
-                           void* recv, float* recv_scales, hipStream_t st) {
+                           void* recv, float* recv_scales, bool affine, hipStream_t st) {
     if (d.Na == 0) return hipSuccess;
     const int L = d.row_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
+    if (affine) {
+        launch_kernel(exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), ws.send_pos, ws.recv_pos,
+                      send_scales, recv_scales, reinterpret_cast<const uint4*>(ws.send_meta),
+                      reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales, d.k, d.T, token_grid(d, slices, true));
+        return hipGetLastError();
+    }
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
     launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
@@ -165,12 +208,16 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
 }
 
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out, uint16_t* comb,
-                                   hipStream_t st) {
+                                   bool affine, hipStream_t st) {
     if (d.Na == 0) return hipSuccess;
     const int L = d.out_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    if (streaming(d, 2LL * d.Na * 16LL * L))
+    if (affine)
+        launch_kernel(reverse_exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L, d.k,
+                      d.T, token_grid(d, slices, true));
+    else if (streaming(d, 2LL * d.Na * 16LL * L))
         launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                       reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L, slices);
     else

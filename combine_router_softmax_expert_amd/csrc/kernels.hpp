@@ -43,10 +43,16 @@ constexpr long long kStreamingBytes = 128LL << 20;
 // id loads fit (kMaxIdsPerThread per thread).
 enum class CountPath { kAuto = 0, kSeparate = 1, kFused = 2 };
 
+// Workgroup layout of the kernels after the pack: kAuto takes the token-affine
+// layout for cache-resident problems (token_affine), kRows always walks rows,
+// kTokens always takes the token-affine layout.
+enum class Layout { kAuto = 0, kRows = 1, kTokens = 2 };
+
 struct Dims {
     int P, Tp, T, E, Ep, k, H;
     CachePolicy policy;
     CountPath count_path;
+    Layout layout;
     bool fp8;
     long long Na;          // T * k
     int row_units;         // 16-byte units per dispatched row (2H/16 or H/16)
@@ -88,22 +94,21 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
                                hipStream_t st);
 hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids, const void* gathered,
                          const float* gathered_scales, void* recv, float* recv_scales, hipStream_t st);
+// affine: the token-affine layout (token_affine(d) must hold), else row grids.
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
-                           void* recv, float* recv_scales, hipStream_t st);
+                           void* recv, float* recv_scales, bool affine, hipStream_t st);
 hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales,
-                       uint16_t* out, hipStream_t st);
+                       uint16_t* out, bool affine, hipStream_t st);
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out,
-                                   uint16_t* comb, hipStream_t st);
+                                   uint16_t* comb, bool affine, hipStream_t st);
 // direct: rows = the expert output, read through recv_pos; else rows = the combine buffer
 hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
-                         bool direct, hipStream_t st);
+                         bool direct, bool affine, hipStream_t st);
 
 inline bool streaming(const Dims& d, long long bytes) {
     return d.policy == CachePolicy::kStreaming || (d.policy == CachePolicy::kAuto && bytes >= kStreamingBytes);
 }
 
-// Threads per block for a row of `n` per-thread work items: the whole row when it
-// fits in 512 threads, else a divisor of n from 512 down to 256, else 256.
 // Grid of a row kernel: rows x slices workgroups in one dimension, the slices of
 // a row adjacent, so that workgroups issued together cover consecutive bytes
 // (measured on gfx950 with 14 KiB rows: a gathering copy 5.6 -> 6.0 TB/s and
@@ -111,6 +116,8 @@ inline bool streaming(const Dims& d, long long bytes) {
 // shape limits keep rows x slices x block below 2^32 work-items.
 inline dim3 row_grid(long long rows, int slices) { return dim3((unsigned)(rows * slices)); }
 
+// Threads per block for a row of `n` per-thread work items: the whole row when it
+// fits in 512 threads, else a divisor of n from 512 down to 256, else 256.
 inline int pick_block(long long n) {
     if (n <= 512) return (int)((n + 63) / 64 * 64);
     for (int b = 512; b >= 256; b -= 64)
@@ -124,5 +131,32 @@ bool count_is_single(const Dims& d);
 // True when launch_pack counts and ranks the assignments itself and writes the
 // counts and offsets too (launch_count and launch_scan are then not needed).
 bool pack_counts(const Dims& d);
+
+// Token-affine layout.  Workgroup w runs on XCD w mod 8 (workgroups are handed
+// out round-robin over the 8 XCDs), and the lines a kernel writes stay in that
+// XCD's L2 for the next kernel: rereading 14.7 MB there took half the time of
+// rereading it from another XCD on gfx950.  The pack's workgroup for token group
+// g (its tokens_per_block tokens) and slice s runs on XCD (g * slices + s) mod 8;
+// in this layout every later kernel serves token group g, slice s on that XCD
+// again, so each reads what the previous one wrote through its own L2.  It needs
+// bf16 rows (dispatch and output rows then have the same slices) and pays when
+// an output buffer fits well inside the L2s; token_affine says whether a ctx
+// allows it (not under Layout::kRows).  The library takes it after a direct
+// dispatch (measured at 128 tokens x top-8 x 7168: step 24.8 -> 23.9 us); after
+// the base dispatch, whose exchange and reverse exchange then have to load
+// their positions before their rows, it measured no faster (33.0 against 33.3
+// us) and is used only under Layout::kTokens.
+constexpr long long kAffineBytes = 24LL << 20;
+bool token_affine(const Dims& d);
+
+// The grid of a token-affine kernel: `rounds` rounds of 2^m_log2 workgroups (a
+// power of two at least groups * slices and 8); within a round, workgroup
+// g * slices + s serves token group g, slice s, the rest exit.  Round r is slot
+// r >> tpb_log2 (0 for per-token kernels) of token g * 2^tpb_log2 + (r & mask).
+struct TokenGrid {
+    int groups, slices, tpb_log2, m_log2, rounds;
+    dim3 grid() const { return dim3((unsigned)rounds << m_log2); }
+};
+TokenGrid token_grid(const Dims& d, int slices, bool per_assignment);
 
 }  // namespace moe

@@ -66,17 +66,20 @@ __device__ __forceinline__ void load_row(const uint4* __restrict__ x, int t, int
     }
 }
 
-// Handle record, position arrays and (base form) the send <-> receive maps of
-// assignment a = t*k + j; called by the first slice only, after the block's
-// barrier (a barrier waits for the block's outstanding global stores, so stores
-// issued before it would sit on the critical path).
+// Position arrays, and from the first slice the handle record and (base form)
+// the send <-> receive maps, of assignment a = t*k + j; called after the
+// block's barrier (a barrier waits for the block's outstanding global stores,
+// so stores issued before it would sit on the critical path).  Every slice
+// writes the (identical) positions, so that the token-affine kernels find them
+// in the L2 of the XCD that serves their slice.
 template <bool DIRECT>
 __device__ __forceinline__ void write_handle(int a, int t, int s, int Tp, int j, int e, int Ep, int p, int q,
-                                             float weight, HandleRecord* __restrict__ dst_meta,
+                                             float weight, bool first_slice, HandleRecord* __restrict__ dst_meta,
                                              int32_t* __restrict__ send_to_recv, int32_t* __restrict__ recv_to_send,
                                              int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos) {
     send_pos[a] = p;
     recv_pos[a] = q;
+    if (!first_slice) return;
     if (!DIRECT) {
         send_to_recv[p] = q;
         recv_to_send[q] = p;
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
     }
     lds_barrier();
     store_rows<FP8, NTS>(xa, xb, pos, k, L, u, dst, dst_scales);
-    if (tid < k && slice == 0)
-        write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send, send_pos,
-                             recv_pos);
+    if (tid < k)
+        write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, slice == 0, dst_meta, send_to_recv, recv_to_send,
+                             send_pos, recv_pos);
 }
 
 // Positions and receive-side handle records only (no rows), one thread per
@@ -212,7 +215,8 @@ __global__ __launch_bounds__(256) void handle_kernel(const int32_t* __restrict__
     const int br = bucket_rank[a];
     const int p = send_off[s * E + e] + br;
     const int q = recv_off[s * E + e] + br;
-    write_handle<true>(a, t, s, Tp, a - t * k, e, Ep, p, q, w[a], recv_meta, nullptr, nullptr, send_pos, recv_pos);
+    write_handle<true>(a, t, s, Tp, a - t * k, e, Ep, p, q, w[a], true, recv_meta, nullptr, nullptr, send_pos,
+                       recv_pos);
 }
 
 // All-gather of the tokens ("Expert Parallel: MoE Token ...", section "为什么不用
@@ -316,11 +320,12 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
     }
 }
 
-// Grid of P + ceil(T / TPB) rows of slices (row_grid): row s < P, slice 0,
-// writes rank s's counts and offsets (the other slices of those rows exit); row P + b packs
-// tokens b*TPB .. b*TPB + TPB - 1 (all on one rank: TPB divides T/P), whose
-// TPB * k <= 32 assignments ("slots") share one counting pass.  The counting
-// blocks come first so they run alongside the packing ones.
+// Grid of ceil(T / TPB) + P rows of slices (row_grid): row b < ceil(T / TPB)
+// packs tokens b*TPB .. b*TPB + TPB - 1 (all on one rank: TPB divides T/P),
+// whose TPB * k <= 32 assignments ("slots") share one counting pass; row
+// ceil(T / TPB) + s, slice 0, writes rank s's counts and offsets (the other
+// slices of those rows exit).  The packing rows come first, so that workgroup
+// b * slices + slice runs on the XCD the token-affine layout expects.
 //
 // For slot (t, j) with expert e on rank s, and t0 the block's first token:
 //   recv_pos = #{a : id_a < e} + #{a < t0*k : id_a = e} + c
@@ -350,12 +355,14 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     const auto [b, slice] = row_slice(slices);
     const int tid = threadIdx.x, bs = blockDim.x;
     const int Na = T * k;
-    if (b < P) {
+    const int groups = (T + TPB - 1) / TPB;
+    if (b >= groups) {
         if (slice == 0)
-            rank_counts<MI>(ids, b, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off, recv_off);
+            rank_counts<MI>(ids, b - groups, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off,
+                            recv_off);
         return;
     }
-    const int t0 = (b - P) * TPB;
+    const int t0 = b * TPB;
     const int ntok = min(TPB, T - t0);
     const int nslots = ntok * k;               // <= 32 by the launch condition
     const int s = t0 / Tp;                     // the block's rank
@@ -419,10 +426,10 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
 #pragma unroll
     for (int i = 0; i < TPB; ++i)
         if (ROWS && i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
-    if (tid < nslots && slice == 0) {
+    if (tid < nslots) {
         const int t = t0 + tid / k;
-        write_handle<DIRECT>(t0k + tid, t, s, Tp, tid % k, my_e, Ep, p, q, wt, dst_meta, send_to_recv, recv_to_send,
-                             send_pos, recv_pos);
+        write_handle<DIRECT>(t0k + tid, t, s, Tp, tid % k, my_e, Ep, p, q, wt, slice == 0, dst_meta, send_to_recv,
+                             recv_to_send, send_pos, recv_pos);
     }
 }
 
@@ -460,6 +467,27 @@ bool pack_counts(const Dims& d) {
     // workgroups reading 4096 ids each)
     if (d.Na > (long long)kMaxIdsPerThread * B) return false;
     return d.count_path == CountPath::kFused || blocks * d.Na <= (1LL << 24);
+}
+
+bool token_affine(const Dims& d) {
+    if (d.fp8 || d.T == 0) return false;   // FP8 dispatch rows and bf16 output rows have different slices
+    if (d.layout == Layout::kRows) return false;
+    if (d.layout == Layout::kAuto && d.Na * 2LL * d.H > kAffineBytes) return false;
+    const int B = pick_block(d.row_units);
+    const TokenGrid g = token_grid(d, (d.row_units + B - 1) / B, true);
+    return ((long long)g.rounds << g.m_log2) * B < (1LL << 32);   // one grid dimension
+}
+
+TokenGrid token_grid(const Dims& d, int slices, bool per_assignment) {
+    const int tpb = pack_counts(d) ? tokens_per_block(d) : 1;   // tokens per packing workgroup: 1, 2 or 4
+    TokenGrid g;
+    g.tpb_log2 = tpb == 4 ? 2 : tpb == 2 ? 1 : 0;
+    g.groups = (d.T + tpb - 1) / tpb;
+    g.slices = slices;
+    g.m_log2 = 3;
+    while ((1LL << g.m_log2) < (long long)g.groups * slices) ++g.m_log2;
+    g.rounds = (per_assignment ? d.k : 1) << g.tpb_log2;
+    return g;
 }
 
 hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, const float* w, const Workspace& ws,

@@ -20,11 +20,21 @@ namespace {
 // run in slot order.
 constexpr int kChunk = 8;
 
-template <bool NTL, bool NTS, bool DIRECT>
+// AFFINE: the token-affine grid (token_affine), which serves token t's slice on
+// the XCD whose L2 holds that token's rows; else a row grid over the tokens.
+template <bool NTL, bool NTS, bool DIRECT, bool AFFINE>
 __global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
                                                      const float* __restrict__ w, uint4* __restrict__ y, int k, int L,
-                                                     int slices) {
-    const auto [t, slice] = row_slice(slices);
+                                                     int slices, int T, TokenGrid tg) {
+    int t, slice;
+    if constexpr (AFFINE) {
+        int j;
+        if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    } else {
+        const RowSlice rs = row_slice(slices);
+        t = rs.row;
+        slice = rs.slice;
+    }
     const int u = slice * blockDim.x + threadIdx.x;
     if (u >= L) return;
     float acc[8];
@@ -57,16 +67,23 @@ __global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ r
 }  // namespace
 
 hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
-                         bool direct, hipStream_t st) {
+                         bool direct, bool affine, hipStream_t st) {
     if (d.T == 0) return hipSuccess;
     const int L = d.out_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
+    if (affine) {
+        const TokenGrid tg = token_grid(d, slices, false);
+        auto kernel = direct ? reduce_kernel<false, false, true, true> : reduce_kernel<false, false, false, true>;
+        launch_kernel(kernel, tg.grid(), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
+                      reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, tg);
+        return hipGetLastError();
+    }
     const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
-    auto kernel = direct ? (nt ? reduce_kernel<true, true, true> : reduce_kernel<false, false, true>)
-                         : (nt ? reduce_kernel<true, true, false> : reduce_kernel<false, false, false>);
+    auto kernel = direct ? (nt ? reduce_kernel<true, true, true, false> : reduce_kernel<false, false, true, false>)
+                         : (nt ? reduce_kernel<true, true, false, false> : reduce_kernel<false, false, false, false>);
     launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
-                  reinterpret_cast<uint4*>(y), d.k, L, slices);
+                  reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, TokenGrid{});
     return hipGetLastError();
 }
 

@@ -15,6 +15,15 @@
 namespace moe {
 namespace {
 
+// One 16-byte unit of a bf16 row times m_e, rounded once to bf16.
+__device__ __forceinline__ uint4 scale_bf16_unit(const uint4& c, float m) {
+    float f[8];
+    unpack8_bf16(c, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] * m;
+    return pack8_bf16(f);
+}
+
 // bf16 rows: one lane per 16-byte unit in and out.  e4m3 rows: a lane reads 16
 // codes as two 8-byte pieces, 64 pieces apart, and writes their two 16-byte
 // outputs, so that each wave-wide store covers 1 KiB contiguously (one 16-byte
@@ -67,22 +76,45 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
         const int r = owner_rank(rank_recv_off, P, q);
         const float m = (float)(E + r * Ep + local) / (float)E;
         if (u >= L) return;
-        float f[8];
-        unpack8_bf16(c, f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = f[i] * m;
-        st16<NTS>(&out[(size_t)q * L + u], pack8_bf16(f));
+        st16<NTS>(&out[(size_t)q * L + u], scale_bf16_unit(c, m));
     }
+}
+
+// Token-affine form for bf16 rows (token_affine): workgroup (t, j, slice) scales
+// receive row recv_pos[t*k + j] on the XCD whose L2 holds what the exchange (or
+// the direct pack) wrote there.
+__global__ __launch_bounds__(512) void stub_affine_kernel(const uint4* __restrict__ recv,
+                                                          const HandleRecord* __restrict__ meta,
+                                                          const int32_t* __restrict__ rank_recv_off,
+                                                          const int32_t* __restrict__ recv_pos, uint4* __restrict__ out,
+                                                          int P, int E, int Ep, int L, int k, int T, TokenGrid tg) {
+    int t, j, slice;
+    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    const int q = recv_pos[t * k + j];
+    const int u = slice * blockDim.x + threadIdx.x;
+    const uint4 c = recv[(size_t)q * L + min(u, L - 1)];
+    const int local = meta[q].local_expert;
+    __builtin_amdgcn_sched_barrier(0);
+    const int r = owner_rank(rank_recv_off, P, q);
+    const float m = (float)(E + r * Ep + local) / (float)E;
+    if (u < L) out[(size_t)q * L + u] = scale_bf16_unit(c, m);
 }
 
 }  // namespace
 
 hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, const float* recv_scales, uint16_t* out,
-                       hipStream_t st) {
+                       bool affine, hipStream_t st) {
     if (d.Na == 0) return hipSuccess;
     const int L = d.row_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
+    if (affine) {   // bf16 rows
+        launch_kernel(stub_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+                      reinterpret_cast<const uint4*>(recv), reinterpret_cast<const HandleRecord*>(ws.recv_meta),
+                      ws.rank_recv_off, ws.recv_pos, reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, d.k, d.T,
+                      token_grid(d, slices, true));
+        return hipGetLastError();
+    }
     const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
     // streaming: e4m3 rows load and store nontemporally (stub 224 -> 231 us but the reverse exchange
     // after it 320 -> 307 us at 65536 rows: no dirty lines left behind), bf16 rows store nontemporally

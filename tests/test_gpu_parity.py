@@ -75,6 +75,18 @@ def test_workload_parity_other_cache_policy(orc, monkeypatch, policy, name):
     _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {policy}")
 
 
+@pytest.mark.parametrize("layout,name,direct", [("rows", "c1", False), ("rows", "c2", False), ("rows", "c2", True),
+                                                ("tokens", "c4", False), ("tokens", "c4", True)])
+def test_workload_parity_other_layout(orc, monkeypatch, layout, name, direct):
+    # cache-resident bf16 problems serve each token's rows on the XCD that packed
+    # them (token-affine layout), larger ones walk rows; force the other layout
+    monkeypatch.setenv("MOE_EP_LAYOUT", layout)
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    _full_parity(orc, orc.Shape.of(w), inp["x"], logits=inp["logits"], label=f"{name} {layout} layout",
+                 direct=direct)
+
+
 @pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True), ("c3", False)])
 def test_workload_parity_separate_count(orc, monkeypatch, name, direct):
     # small problems rank their assignments inside the pack kernel; force the
@@ -197,14 +209,22 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("policy,count,direct", [("auto", "auto", False), ("streaming", "auto", False),
-                                                 ("auto", "auto", True), ("auto", "separate", False),
-                                                 ("auto", "fused", True), ("auto", "auto", "allgather"),
-                                                 ("streaming", "separate", "allgather")])
+@pytest.mark.parametrize("policy,count,direct,layout", [("auto", "auto", False, "auto"),
+                                                        ("streaming", "auto", False, "auto"),
+                                                        ("auto", "auto", True, "auto"),
+                                                        ("auto", "separate", False, "auto"),
+                                                        ("auto", "fused", True, "auto"),
+                                                        ("auto", "auto", "allgather", "auto"),
+                                                        ("streaming", "separate", "allgather", "auto"),
+                                                        ("auto", "auto", False, "rows"),
+                                                        ("auto", "separate", True, "rows"),
+                                                        ("auto", "auto", False, "tokens"),
+                                                        ("auto", "separate", True, "tokens")])
 @pytest.mark.parametrize("name,P,Tp,E,k,H,fp8", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, count, direct):
+def test_edge_shapes(orc, monkeypatch, name, P, Tp, E, k, H, fp8, policy, count, direct, layout):
     monkeypatch.setenv("MOE_EP_CACHE_POLICY", policy)
     monkeypatch.setenv("MOE_EP_COUNT_PATH", count)
+    monkeypatch.setenv("MOE_EP_LAYOUT", layout)
     allgather = direct == "allgather"
     direct = direct is True
     sh = orc.Shape(P, P * Tp, E, k, H, fp8)
