@@ -107,7 +107,8 @@ KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the pat
     ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"),
     ("allgather_kernel", "allgather"), ("handle_kernel", "handles"), ("select_kernel", "select"),
     ("select_scatter_kernel", "select"), ("reverse_exchange_", "reverse_exchange"),
-    ("exchange_kernel", "exchange"), ("stub_kernel", "stub"), ("reduce_kernel", "reduce"),
+    ("exchange_kernel", "exchange"), ("exchange_affine_kernel", "exchange"), ("stub_kernel", "stub"),
+    ("stub_affine_kernel", "stub"), ("reduce_kernel", "reduce"),
 )
 
 
