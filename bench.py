@@ -79,6 +79,13 @@ def metadata_bytes(w) -> int:
     return Na * (16 + 4 + 8) + 2 * Na * 16 + Na * 16
 
 
+def logical_payload_bytes(w) -> int:
+    """The bytes that cross the links once each way: every assignment's dispatched row
+    (the FP8 codes without their scales, else 2H) and its bf16 combine row."""
+    row = w.hidden if w.dispatch_dtype != "bf16" else 2 * w.hidden
+    return w.tokens * w.top_k * (row + 2 * w.hidden)
+
+
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_router_softmax_expert_amd", "csrc")
@@ -481,6 +488,8 @@ def main():
             "ms": round(dc_ms, 5), "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
             "algorithmic_bytes": dc_bytes, "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "logical_payload_bytes": logical_payload_bytes(w),
+            "logical_payload_gbps": round(logical_payload_bytes(w) / (dc_ms * 1e-3) / 1e9, 1),
         },
         "other_mode": None if not extras else {
             "mode": "base" if direct else "direct",

@@ -43,6 +43,9 @@ def test_byte_model_example_payload():
     # the logical payload of the byte-model workload: N_a * H * (1 + 2) bytes
     w = wl.WORKLOADS["c3"]
     assert w.tokens * w.top_k * w.hidden * (1 + 2) == 88_080_384
+    assert bench.logical_payload_bytes(w) == 88_080_384
+    # bf16 dispatch: 2H out and 2H back per assignment (decode workload: 29,360,128 B)
+    assert bench.logical_payload_bytes(wl.WORKLOADS["c2"]) == 29_360_128
 
 
 @pytest.mark.parametrize("rocprof_name,kernel", [
