@@ -189,6 +189,41 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+def routing_stats(ids, num_ranks: int, num_experts: int) -> dict:
+    """The routing's shape from the expert ids [T, k]: per-expert load imbalance
+    (max / mean), empty experts, the share the hottest tenth of the experts takes,
+    per-destination-rank imbalance and the share of assignments that stay on the
+    source rank."""
+    import numpy as np
+    T, k = ids.shape
+    n_e = np.bincount(ids.ravel(), minlength=num_experts)
+    Ep = num_experts // num_ranks
+    dst = ids // Ep
+    src = np.repeat(np.arange(T) // (T // num_ranks), k).reshape(T, k)
+    n_r = np.bincount(dst.ravel(), minlength=num_ranks)
+    top = np.sort(n_e)[::-1][:max(1, num_experts // 10)]
+    return {
+        "expert_imbalance": round(float(n_e.max() / n_e.mean()), 3),
+        "empty_experts": int((n_e == 0).sum()),
+        "top10pct_expert_share": round(float(top.sum() / n_e.sum()), 4),
+        "rank_imbalance": round(float(n_r.max() / n_r.mean()), 3),
+        "local_share": round(float((dst == src).mean()), 4),
+    }
+
+
+def host_info() -> dict:
+    import platform
+    import torch
+    cpu = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "host_cpu": cpu,
+            "host_cores": os.cpu_count()}
+
+
 def cpu_baseline(w, inp, budget_s: float) -> dict:
     """The oracle, as it stands, on one host core over a bounded sample of the workload."""
     import numpy as np
@@ -513,6 +548,8 @@ def main():
         "metadata_bytes_per_step": metadata_bytes(w),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "routing": routing_stats(bufs["topk_ids"].cpu().numpy(), w.num_ranks, w.num_experts),
+        "hardware": host_info(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -8,6 +8,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 from conftest import ROOT
@@ -37,6 +38,16 @@ def test_dispatch_combine_bytes_match_the_closed_form(name, total):
     D = H + 4 * (H // 128) if w.dispatch_dtype != "bf16" else 2 * H
     assert kb["pack_direct"] + kb["reduce_direct"] == 2 * H * T + Na * D + Na * 2 * H + 2 * H * T
     assert kb["count_pack"] == kb["count"] + kb["pack"]
+
+
+def test_routing_stats_on_a_known_routing():
+    # 2 ranks, 4 experts (2 per rank), 4 tokens (2 per rank), top-2
+    ids = np.array([[0, 1], [0, 2], [3, 0], [2, 3]], dtype=np.int32)
+    s = bench.routing_stats(ids, 2, 4)
+    # expert loads 3, 1, 2, 2 (mean 2); rank loads 4, 4; tokens 0-1 on rank 0, 2-3 on rank 1:
+    # local assignments: (0,0) (0,1) (1,0) for rank 0 and (2,3) (3,2) (3,3) for rank 1 -> 6 of 8
+    assert s == {"expert_imbalance": 1.5, "empty_experts": 0, "top10pct_expert_share": 0.375,
+                 "rank_imbalance": 1.0, "local_share": 0.75}
 
 
 def test_byte_model_example_payload():
