@@ -220,7 +220,9 @@ def host_info() -> dict:
             cpu = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "host_cpu": cpu,
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": torch.version.hip, "host_cpu": cpu,
             "host_cores": os.cpu_count()}
 
 
