@@ -4,6 +4,7 @@
 #include "moe_ep.h"
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cstdlib>
 #include <cstring>
@@ -20,6 +21,16 @@ thread_local std::string g_last_error;
 constexpr size_t kAlign = 256;
 constexpr int kFp8Block = 128;   // channels per FP8 scale, per token
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// A roctx range around one library call, so that a rocprofv3 --marker-trace
+// shows each call of the path (route, dispatch and its halves, stub, combine and
+// its halves) around the kernels it launched.
+struct CallRange {
+    explicit CallRange(const char* name) { roctxRangePushA(name); }
+    ~CallRange() { roctxRangePop(); }
+    CallRange(const CallRange&) = delete;
+    CallRange& operator=(const CallRange&) = delete;
+};
 
 struct TimingRecord {
     const char* name;
@@ -298,6 +309,7 @@ int32_t moe_scales_per_row(const moe_ctx* ctx) { return ctx ? ctx->d.scales : 0;
 int64_t moe_num_assignments(const moe_ctx* ctx) { return ctx ? ctx->d.Na : 0; }
 
 moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+    const CallRange range("moe_route_topk");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     if (ctx->d.T == 0) return MOE_OK;
     if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
@@ -309,6 +321,7 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, 
 moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                              void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
                              moe_handle* handle, void* stream) {
+    const CallRange range("moe_dispatch_send");
     if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
     const moe::Dims d = ctx->d;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
@@ -336,6 +349,7 @@ moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* top
 
 moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
                              void* recv_buf, float* recv_scales, void* stream) {
+    const CallRange range("moe_dispatch_recv");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_handle(ctx, handle);
     if (s != MOE_OK) return s;
@@ -363,6 +377,7 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
 moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                         void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
                         void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+    const CallRange range("moe_dispatch");
     if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
     const moe::Dims d = ctx->d;
     // every argument is checked before anything is enqueued
@@ -377,6 +392,7 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
 moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                void* workspace, size_t workspace_bytes, void* recv_buf, float* recv_scales,
                                moe_handle* handle, void* stream) {
+    const CallRange range("moe_dispatch_direct");
     if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
     const moe::Dims d = ctx->d;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
@@ -407,6 +423,7 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
 moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                   void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
                                   void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
+    const CallRange range("moe_dispatch_allgather");
     if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
     const moe::Dims d = ctx->d;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
@@ -442,6 +459,7 @@ moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t
 
 moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf, const float* recv_scales,
                            uint16_t* expert_out, void* stream) {
+    const CallRange range("moe_expert_stub");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_received(ctx, handle, "moe_expert_stub");
     if (s != MOE_OK) return s;
@@ -457,6 +475,7 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
 
 moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                             uint16_t* comb_buf, void* stream) {
+    const CallRange range("moe_combine_send");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_received(ctx, handle, "moe_combine_send");
     if (s != MOE_OK) return s;
@@ -477,6 +496,7 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
 
 moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
                             uint16_t* y, void* stream) {
+    const CallRange range("moe_combine_recv");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_received(ctx, handle, "moe_combine_recv");
     if (s != MOE_OK) return s;
@@ -495,6 +515,7 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
 
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out, const float* topk_w,
                        uint16_t* comb_buf, uint16_t* y, void* stream) {
+    const CallRange range("moe_combine");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_received(ctx, handle, "moe_combine");
     if (s != MOE_OK) return s;
@@ -506,6 +527,7 @@ moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* e
 
 moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                               const float* topk_w, uint16_t* y, void* stream) {
+    const CallRange range("moe_combine_direct");
     if (!ctx) return MOE_ERR_INVALID_ARG;
     moe_status s = check_received(ctx, handle, "moe_combine_direct");
     if (s != MOE_OK) return s;
