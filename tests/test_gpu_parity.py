@@ -414,3 +414,37 @@ def test_no_writes_outside_buffers(orc, monkeypatch, name, P, Tp, E, k, H, fp8, 
     assert np.array_equal(bufs["topk_ids"].cpu().numpy(), o_ids)
     o = orc.run(sh, x_np, ids=o_ids, w=bufs["topk_w"].cpu().numpy())
     assert np.array_equal(bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16), o["y"].view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_direct_dispatch_with_either_combine(orc, name):
+    """After a direct dispatch (token-affine layout at these sizes) both combines, the base one through the
+    combine buffer and the direct one through recv_pos, give y bit for bit equal to the oracle's."""
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    log(f"[direct+either combine] {name}")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    sh = orc.Shape.of(w)
+    ctx = B.Context.for_workload(w)
+    bufs = ctx.allocate()
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    B.moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"])
+    h = B.moe_dispatch_direct(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
+                              bufs["recv_scales"])
+    B.moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"])
+    B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
+    torch.cuda.synchronize()
+    y_base = bufs["y"].view(torch.int16).cpu().numpy().copy()
+    comb = bufs["comb"].view(torch.int16).cpu().numpy().copy()
+    bufs["y"].view(torch.uint8).fill_(0xFF)
+    B.moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"])
+    torch.cuda.synchronize()
+    y_direct = bufs["y"].view(torch.int16).cpu().numpy()
+    ids, wt = bufs["topk_ids"].cpu().numpy(), bufs["topk_w"].cpu().numpy()
+    o = orc.run(sh, inp["x"], ids=ids, w=wt)
+    assert np.array_equal(comb.view(np.uint16), o["comb"].view(np.uint16).reshape(comb.shape))
+    assert np.array_equal(y_base.view(np.uint16), o["y"].view(np.uint16))
+    assert np.array_equal(y_direct.view(np.uint16), o["y"].view(np.uint16))
