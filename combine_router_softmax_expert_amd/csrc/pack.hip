@@ -11,7 +11,7 @@
 // One token per workgroup slice: the token's row is read once (16-byte loads)
 // and written to its k send rows; the FP8 form is computed once per token and
 // copied k times.  FP8: a lane owns 16 channels, 8 lanes a 128-channel block;
-// amax by xor shuffles, scale = amax / 448 (fp32 division), code =
+// amax by DPP moves within the 8 lanes, scale = amax / 448 (fp32 division), code =
 // e4m3(x / scale) (fp32 division, then v_cvt_pk_fp8_f32: nearest even).  The positions of the k
 // assignments are send_off[s][e] + bucket rank and recv_off[s][e] + bucket
 // rank; the first slice also writes the handle record, the position arrays and
@@ -49,6 +49,21 @@ namespace {
 
 constexpr int kMaxIdsPerThread = 16;   // expert ids a thread of the counting form keeps in registers
 constexpr int kMaxRanksPerStore = 32;  // row copies the all-gather writes per pass
+
+// Maximum over each aligned group of 8 lanes, in every lane of the group, by
+// three DPP moves (no LDS traffic): quad_perm [1,0,3,2] and [2,3,0,1] give
+// each quad its maximum, then row_half_mirror (lane i of each group of 8 reads
+// lane 7 - i, which sits in the other quad) combines the two quads.  A group
+// is all active or all inactive, so no lane reads a disabled one.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    return fmaxf(v, dpp_f32<0x141>(v));
+}
 
 // The token's row, loaded before anything else so its latency overlaps the
 // position work (FP8 reads 32 bytes of bf16 per 16-byte output unit).
@@ -112,9 +127,7 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-        amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+        amax = max8(amax);
         const float scale = amax / 448.0f;
         uint32_t q[4];
         if (amax == 0.0f) {                       // all zeros: scale 0, codes keep each zero's sign
