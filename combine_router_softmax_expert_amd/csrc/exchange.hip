@@ -44,7 +44,7 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
         __builtin_amdgcn_sched_barrier(0);
         q = map[b];
     }
-    if (u < L) st16<GATHER>(&recv[(size_t)q * L + u], v);
+    if (u < L) st16_row<GATHER>(recv, q, L, u, v);
     if (slice == 0) {
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
         if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uin
     __builtin_amdgcn_sched_barrier(0);
     const HandleRecord m = recv_meta[q];
     const long long c = ((long long)m.src_rank * Tp + m.src_token) * k + m.slot;
-    if (u < L) comb[(size_t)c * L + u] = v;
+    if (u < L) st16_row<false>(comb, (int)c, L, u, v);
 }
 
 __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint4* __restrict__ expert_out,
@@ -72,13 +72,15 @@ __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint
     const auto [c, slice] = row_slice(slices);  // combine row t*k + j
     const int q = recv_pos[c];
     const int u = slice * blockDim.x + threadIdx.x;
-    if (u < L) st16<true>(&comb[(size_t)c * L + u], ld16<true>(&expert_out[(size_t)q * L + u]));
+    if (u < L) st16_row<true>(comb, c, L, u, ld16<true>(&expert_out[(size_t)q * L + u]));
 }
 
 // Token-affine forms (cache-resident bf16 problems, token_affine): workgroup
 // (t, j, slice) moves the rows of assignment t*k + j on the XCD whose L2 holds
 // what the previous kernel wrote for that token and slice.  The positions come
-// from the handle (every slice of the pack wrote them), then the row.
+// from the handle (every slice of the pack wrote them), then the row.  Their
+// stores are write-back (plain), not st16_row's write-through: the next kernel
+// reads each line on the same XCD, from that L2.
 __global__ __launch_bounds__(512) void exchange_affine_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
                                                               const int32_t* __restrict__ send_pos,
                                                               const int32_t* __restrict__ recv_pos,
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(512) void select_kernel(const uint4* __restrict__ g
     const int r = owner_rank(rank_recv_off, P, q);
     const HandleRecord m = recv_meta[q];
     const size_t src = (size_t)r * T + (size_t)m.src_rank * Tp + m.src_token;
-    if (u < L) st16<NT>(&recv[(size_t)q * L + u], ld16<NT>(&gathered[src * L + u]));
+    if (u < L) st16_row<NT>(recv, q, L, u, ld16<NT>(&gathered[src * L + u]));
     if (slice == 0)
         for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = gathered_scales[src * nb + x];
 }
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(512) void select_scatter_kernel(const uint4* __rest
         const int a = t * k + j;
         if (ids[a] / Ep != r) continue;        // uniform: the same slot in every lane
         const int q = recv_pos[a];
-        if (u < L) st16<NT>(&recv[(size_t)q * L + u], v);
+        if (u < L) st16_row<NT>(recv, q, L, u, v);
         if (slice == 0)
             for (int x = threadIdx.x; x < nb; x += blockDim.x)
                 recv_scales[(size_t)q * nb + x] = gathered_scales[(size_t)g * nb + x];

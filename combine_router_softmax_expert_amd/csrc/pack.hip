@@ -163,11 +163,11 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
         const int nb = L / 8;
         for (int j = 0; j < k; ++j) {
             const int p = pos[j];
-            st16<NTS>(&dst[(size_t)p * L + u], out);
+            st16_row<NTS>(dst, p, L, u, out);
             if ((u & 7) == 0) dst_scales[(size_t)p * nb + (u >> 3)] = scale;
         }
     } else {
-        for (int j = 0; j < k; ++j) st16<NTS>(&dst[(size_t)pos[j] * L + u], xa);
+        for (int j = 0; j < k; ++j) st16_row<NTS>(dst, pos[j], L, u, xa);
     }
 }
 

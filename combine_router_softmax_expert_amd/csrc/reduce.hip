@@ -61,7 +61,7 @@ __global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ r
             }
         }
     }
-    st16<NTS>(&y[(size_t)t * L + u], pack8_bf16(acc));
+    st16_row<NTS>(y, t, L, u, pack8_bf16(acc));
 }
 
 }  // namespace

@@ -59,14 +59,14 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
             unpack4_e4m3(a.y, f + 4);
 #pragma unroll
             for (int i = 0; i < 8; ++i) f[i] = (f[i] * sa) * m;
-            st16<NTS>(&out[(size_t)q * n + p0], pack8_bf16(f));
+            st16_row<NTS>(out, q, n, p0, pack8_bf16(f));
         }
         if (p1 < n) {
             unpack4_e4m3(b.x, f);
             unpack4_e4m3(b.y, f + 4);
 #pragma unroll
             for (int i = 0; i < 8; ++i) f[i] = (f[i] * sb) * m;
-            st16<NTS>(&out[(size_t)q * n + p1], pack8_bf16(f));
+            st16_row<NTS>(out, q, n, p1, pack8_bf16(f));
         }
     } else {
         const int u = slice * blockDim.x + threadIdx.x;         // 16-byte unit
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
         const int r = owner_rank(rank_recv_off, P, q);
         const float m = (float)(E + r * Ep + local) / (float)E;
         if (u >= L) return;
-        st16<NTS>(&out[(size_t)q * L + u], scale_bf16_unit(c, m));
+        st16_row<NTS>(out, q, L, u, scale_bf16_unit(c, m));
     }
 }
 
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512) void stub_affine_kernel(const uint4* __restric
     __builtin_amdgcn_sched_barrier(0);
     const int r = owner_rank(rank_recv_off, P, q);
     const float m = (float)(E + r * Ep + local) / (float)E;
-    if (u < L) out[(size_t)q * L + u] = scale_bf16_unit(c, m);
+    if (u < L) out[(size_t)q * L + u] = scale_bf16_unit(c, m);   // write-back: read next on this XCD
 }
 
 }  // namespace
