@@ -183,10 +183,17 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
     dst = torch.empty_like(src)
+    torch.neg(src, out=dst)                      # warm
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
     for _ in range(reps):
         torch.neg(src, out=dst)
+    stop.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+    ms = start.elapsed_time(stop) / reps
+    # the copy's own rate: a practical ceiling for the path's copy kernels on this GPU
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps + 1, "ms_per_copy": round(ms, 4),
+                      "copy_tbps": round(2 * nbytes / (ms * 1e-3) / 1e12, 3)}))
 
 
 def routing_stats(ids, num_ranks: int, num_experts: int) -> dict:
