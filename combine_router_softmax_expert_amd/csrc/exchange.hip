@@ -32,23 +32,28 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
                                                        uint4* __restrict__ recv_meta, int L, int nb, int slices) {
     const auto [b, slice] = row_slice(slices);
     const int u = slice * blockDim.x + threadIdx.x;
-    int p, q;
-    uint4 v;
-    if (GATHER) {                               // the source row comes from the map
-        q = b;
-        p = map[b];
-        if (u < L) v = ld16<true>(&send[(size_t)p * L + u]);
-    } else {                                    // the row's data is loaded before its destination
-        p = b;                                  // index, so the two memory round trips overlap
-        if (u < L) v = send[(size_t)p * L + u];
-        __builtin_amdgcn_sched_barrier(0);
-        q = map[b];
-    }
+    const bool copies_scale = slice == 0 && (int)threadIdx.x < nb;
+    const bool copies_record = slice == 0 && threadIdx.x == blockDim.x - 1;
+    // The map entry is uniform, so it loads through the scalar cache (the
+    // scatter form's row load does not depend on it).  The row's first scales
+    // and its record load together with the row, before any store: vmcnt
+    // counts loads and stores in order, so a load issued after the row's store
+    // would first wait for that store to complete.
+    const int m = map[b];
+    const int p = GATHER ? m : b;               // gather: the source row comes from the map
+    const int q = GATHER ? b : m;               // scatter: the destination row does
+    uint4 v, rec;
+    float sc;
+    if (u < L) v = ld16<GATHER>(&send[(size_t)p * L + u]);
+    if (copies_scale) sc = send_scales[(size_t)p * nb + threadIdx.x];
+    if (copies_record) rec = send_meta[p];
     if (u < L) st16_row<GATHER>(recv, q, L, u, v);
-    if (slice == 0) {
-        for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
-        if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
+    if (copies_scale) {
+        recv_scales[(size_t)q * nb + threadIdx.x] = sc;
+        for (int x = threadIdx.x + blockDim.x; x < nb; x += blockDim.x)   // rows with more scales than threads
+            recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
     }
+    if (copies_record) recv_meta[q] = rec;
 }
 
 __global__ __launch_bounds__(512) void reverse_exchange_scatter_kernel(const uint4* __restrict__ expert_out,
@@ -94,11 +99,20 @@ __global__ __launch_bounds__(512) void exchange_affine_kernel(const uint4* __res
     const int a = t * k + j;
     const int p = send_pos[a], q = recv_pos[a];
     const int u = slice * blockDim.x + threadIdx.x;
-    if (u < L) recv[(size_t)q * L + u] = send[(size_t)p * L + u];
-    if (slice == 0) {
-        for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
-        if (threadIdx.x == blockDim.x - 1) recv_meta[q] = send_meta[p];
+    const bool copies_scale = slice == 0 && (int)threadIdx.x < nb;
+    const bool copies_record = slice == 0 && threadIdx.x == blockDim.x - 1;
+    uint4 v, rec;
+    float sc;
+    if (u < L) v = send[(size_t)p * L + u];
+    if (copies_scale) sc = send_scales[(size_t)p * nb + threadIdx.x];   // loads before stores, as in exchange_kernel
+    if (copies_record) rec = send_meta[p];
+    if (u < L) recv[(size_t)q * L + u] = v;
+    if (copies_scale) {
+        recv_scales[(size_t)q * nb + threadIdx.x] = sc;
+        for (int x = threadIdx.x + blockDim.x; x < nb; x += blockDim.x)
+            recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
     }
+    if (copies_record) recv_meta[q] = rec;
 }
 
 __global__ __launch_bounds__(512) void reverse_exchange_affine_kernel(const uint4* __restrict__ expert_out,
@@ -130,9 +144,17 @@ __global__ __launch_bounds__(512) void select_kernel(const uint4* __restrict__ g
     const int r = owner_rank(rank_recv_off, P, q);
     const HandleRecord m = recv_meta[q];
     const size_t src = (size_t)r * T + (size_t)m.src_rank * Tp + m.src_token;
-    if (u < L) st16_row<NT>(recv, q, L, u, ld16<NT>(&gathered[src * L + u]));
-    if (slice == 0)
-        for (int x = threadIdx.x; x < nb; x += blockDim.x) recv_scales[(size_t)q * nb + x] = gathered_scales[src * nb + x];
+    const bool copies_scale = slice == 0 && (int)threadIdx.x < nb;
+    uint4 v;
+    float sc;
+    if (u < L) v = ld16<NT>(&gathered[src * L + u]);
+    if (copies_scale) sc = gathered_scales[src * nb + threadIdx.x];   // loads before stores, as in exchange_kernel
+    if (u < L) st16_row<NT>(recv, q, L, u, v);
+    if (copies_scale) {
+        recv_scales[(size_t)q * nb + threadIdx.x] = sc;
+        for (int x = threadIdx.x + blockDim.x; x < nb; x += blockDim.x)
+            recv_scales[(size_t)q * nb + x] = gathered_scales[src * nb + x];
+    }
 }
 
 // Source-walking form of the same pick, for when every rank's copy is mostly
