@@ -82,11 +82,13 @@ __device__ __forceinline__ void load_row(const uint4* __restrict__ x, int t, int
 }
 
 // Position arrays, and from the first slice the handle record and (base form)
-// the send <-> receive maps, of assignment a = t*k + j; called after the
-// block's barrier (a barrier waits for the block's outstanding global stores,
-// so stores issued before it would sit on the critical path).  Every slice
-// writes the (identical) positions, so that the token-affine kernels find them
-// in the L2 of the XCD that serves their slice.
+// the send <-> receive maps, of assignment a = t*k + j.  Called by the lanes
+// that own the slots as soon as they have the positions, before the block's
+// LDS-only barrier (which does not wait for global stores) and before the row
+// stores: issued after the row stores, these stores reused the row stores'
+// registers, so the compiler first waited for all k row stores to complete.
+// Every slice writes the (identical) positions, so that the token-affine
+// kernels find them in the L2 of the XCD that serves their slice.
 template <bool DIRECT>
 __device__ __forceinline__ void write_handle(int a, int t, int s, int Tp, int j, int e, int Ep, int p, int q,
                                              float weight, bool first_slice, HandleRecord* __restrict__ dst_meta,
@@ -202,12 +204,11 @@ __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, 
         p = send_off[s * E + e] + br;
         q = recv_off[s * E + e] + br;
         pos[tid] = DIRECT ? q : p;
+        write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, slice == 0, dst_meta, send_to_recv, recv_to_send,
+                             send_pos, recv_pos);
     }
     lds_barrier();
     store_rows<FP8, NTS>(xa, xb, pos, k, L, u, dst, dst_scales);
-    if (tid < k)
-        write_handle<DIRECT>(a, t, s, Tp, tid, e, Ep, p, q, wt, slice == 0, dst_meta, send_to_recv, recv_to_send,
-                             send_pos, recv_pos);
 }
 
 // Positions and receive-side handle records only (no rows), one thread per
@@ -433,17 +434,14 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
             q = min(q, Na - 1);                 // no-ops for valid input; keep every write in bounds
             p = min(p, hi - 1);
             pos[tid] = DIRECT ? q : p;
+            write_handle<DIRECT>(t0k + tid, t0 + tid / k, s, Tp, tid % k, my_e, Ep, p, q, wt, slice == 0, dst_meta,
+                                 send_to_recv, recv_to_send, send_pos, recv_pos);
         }
     }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < TPB; ++i)
         if (ROWS && i < ntok) store_rows<FP8, false>(xa[i], xb[i], pos + i * k, k, L, u, dst, dst_scales);
-    if (tid < nslots) {
-        const int t = t0 + tid / k;
-        write_handle<DIRECT>(t0k + tid, t, s, Tp, tid % k, my_e, Ep, p, q, wt, slice == 0, dst_meta, send_to_recv,
-                             recv_to_send, send_pos, recv_pos);
-    }
 }
 
 }  // namespace
