@@ -277,8 +277,10 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 1000 steps: at decode size one step is ~31 us, and a timed region of a few
+    # ms let one host or GPU hiccup move the mean by 10-20%
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--mode", default="base", choices=["base", "direct"],
                     help="base: pack into send buffers + exchange copies; direct: pack straight into the "
