@@ -334,19 +334,18 @@ def main():
 
     direct = args.mode == "direct"
 
+    # Each form's calls with their arguments checked and marshalled once (binding.PreparedPath):
+    # the same library calls and kernels as binding.run_path without its per-call Python work,
+    # which at decode size cost more host time per step than the GPU needs for the step.
+    paths = {d: B.PreparedPath(ctx, bufs, x, logits, stream, direct=d) for d in (False, True)}
+    dcs = {d: B.PreparedPath(ctx, bufs, x, None, stream, direct=d, stages="dispatch_combine") for d in (False, True)}
+
     def step(direct=direct):
-        B.run_path(ctx, bufs, x, logits, stream, direct=direct)
+        paths[direct]()
 
     def dispatch_combine(direct=direct):
         """Dispatch and combine alone (routing ids/weights and expert outputs from earlier steps)."""
-        if direct:
-            h = B.moe_dispatch_direct(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["recv"],
-                                      bufs["recv_scales"], stream)
-            B.moe_combine_direct(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["y"], stream)
-        else:
-            h = B.moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
-                               bufs["send_scales"], bufs["recv"], bufs["recv_scales"], stream)
-            B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+        dcs[direct]()
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
