@@ -410,10 +410,8 @@ def main():
         # the all-gather dispatcher (with the base combine) on the same data
         gathered, gathered_scales = ctx.allocate_gathered(dev)
 
-        def allgather_dc():
-            h = B.moe_dispatch_allgather(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], gathered,
-                                         gathered_scales, bufs["recv"], bufs["recv_scales"], stream)
-            B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"], stream)
+        allgather_dc = B.PreparedPath(ctx, bufs, x, None, stream, stages="dispatch_combine", gathered=gathered,
+                                      gathered_scales=gathered_scales)
 
         for _ in range(args.warmup):
             allgather_dc()
@@ -421,7 +419,7 @@ def main():
         B.moe_timing_begin(ctx)
         timed(allgather_dc, args.steps)
         kt_ag = B.moe_timing_end(ctx)
-        del gathered, gathered_scales
+        del allgather_dc, gathered, gathered_scales
         step()   # leave the buffers as the measured form wrote them
 
     # per-step times with the caches flushed before each step (a 1 GiB write)

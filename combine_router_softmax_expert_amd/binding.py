@@ -370,22 +370,26 @@ class PreparedPath:
     Each call then issues the same calls with the cached arguments: route, dispatch,
     expert stub and combine (``stages="path"``), or dispatch and combine alone
     (``stages="dispatch_combine"``, on the ids and weights already in ``bufs``), in
-    the base or the direct form.  The calls and their kernels are those of
+    the base or the direct form, or with the all-gather dispatcher when its per-rank
+    copies (``gathered``, ``gathered_scales`` from ``Context.allocate_gathered``) are
+    given (base combine).  The calls and their kernels are those of
     ``run_path``; only the per-call Python work goes (at 128 tokens x top-8 x 7168
     it was ~7 us of host time per step, more than the GPU's spare time).  The
     tensors must stay alive and in place while the object is used."""
 
     def __init__(self, ctx: Context, bufs: dict, x, logits=None, stream=None, direct: bool = False,
-                 stages: str = "path"):
+                 stages: str = "path", gathered=None, gathered_scales=None):
         import torch
         if stages not in ("path", "dispatch_combine"):
             raise ValueError(f"stages must be 'path' or 'dispatch_combine', not {stages!r}")
         if x is None or (stages == "path" and logits is None):
             raise ValueError("x, and for the whole path the logits, are required")
+        if gathered is not None and direct:
+            raise ValueError("the all-gather dispatcher has no direct form")
         T, H, k, E, Na = ctx.T, ctx.H, ctx.k, ctx.E, ctx.num_assignments
         rb, nb = ctx.row_bytes, ctx.scales_per_row
         bf16 = (torch.bfloat16, torch.int16)
-        self._keep = (ctx, bufs, x, logits, stream)
+        self._keep = (ctx, bufs, x, logits, stream, gathered, gathered_scales)
         self.handle = MoeHandle()
         h = ctypes.byref(self.handle)
         c = ctx.handle_ptr
@@ -403,7 +407,12 @@ class PreparedPath:
         if stages == "path":
             calls.append((lib.moe_route_topk, (c, _ptr(logits, torch.float32, 4 * T * E, "logits"), ids, w, s),
                           "moe_route_topk"))
-        if direct:
+        if gathered is not None:
+            g = _ptr(gathered, None, ctx.P * T * rb, "gathered")
+            g_sc = _ptr(gathered_scales, torch.float32, 4 * ctx.P * T * nb, "gathered_scales")
+            calls.append((lib.moe_dispatch_allgather, (c, xp, ids, w, ws, ws_bytes, g, g_sc, recv, recv_sc, h, s),
+                          "moe_dispatch_allgather"))
+        elif direct:
             calls.append((lib.moe_dispatch_direct, (c, xp, ids, w, ws, ws_bytes, recv, recv_sc, h, s),
                           "moe_dispatch_direct"))
         else:

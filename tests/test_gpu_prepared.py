@@ -57,6 +57,40 @@ def test_prepared_path_matches_run_path(name, direct):
         assert torch.equal(bufs["y"].view(torch.uint8), want["y"]), (name, direct, i, "dispatch_combine")
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_prepared_allgather_matches_individual_calls(name):
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    log(f"[prepared allgather] {name}")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    ctx = B.Context.for_workload(w)
+    ref, bufs = ctx.allocate(), ctx.allocate()
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    g_ref, gs_ref = ctx.allocate_gathered()
+    g, gs = ctx.allocate_gathered()
+    B.run_path(ctx, ref, x, logits)                  # ids, weights, expert outputs
+    h = B.moe_dispatch_allgather(ctx, x, ref["topk_ids"], ref["topk_w"], ref["workspace"], g_ref, gs_ref,
+                                 ref["recv"], ref["recv_scales"])
+    B.moe_combine(ctx, h, ref["expert_out"], ref["topk_w"], ref["comb"], ref["y"])
+    torch.cuda.synchronize()
+    for key in ("topk_ids", "topk_w", "expert_out"):
+        bufs[key].copy_(ref[key])
+    for key in ("recv", "comb", "y"):
+        bufs[key].view(torch.uint8).fill_(0xA5)
+    ag = B.PreparedPath(ctx, bufs, x, None, stages="dispatch_combine", gathered=g, gathered_scales=gs)
+    ag()
+    ag()
+    torch.cuda.synchronize()
+    for key in ("recv", "comb", "y"):
+        assert torch.equal(bufs[key].view(torch.uint8), ref[key].view(torch.uint8)), (name, key)
+    assert torch.equal(g.view(torch.uint8), g_ref.view(torch.uint8)), name
+    with pytest.raises(ValueError):
+        B.PreparedPath(ctx, bufs, x, None, direct=True, stages="dispatch_combine", gathered=g, gathered_scales=gs)
+
+
 def test_prepared_path_rejects_bad_tensors():
     import torch
     from combine_router_softmax_expert_amd import binding as B
