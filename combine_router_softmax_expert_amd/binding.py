@@ -393,7 +393,6 @@ class PreparedPath:
         self.handle = MoeHandle()
         h = ctypes.byref(self.handle)
         c = ctx.handle_ptr
-        s = _stream(stream)
         ids = _ptr(bufs["topk_ids"], torch.int32, 4 * T * k, "topk_ids")
         w = _ptr(bufs["topk_w"], torch.float32, 4 * T * k, "topk_w")
         ws = _ptr(bufs["workspace"], None, ctx.workspace_bytes, "workspace")
@@ -403,6 +402,7 @@ class PreparedPath:
         recv_sc = _ptr(bufs["recv_scales"], torch.float32, 4 * Na * nb, "recv_scales")
         out = _ptr(bufs["expert_out"], bf16, 2 * Na * H, "expert_out")
         y = _ptr(bufs["y"], bf16, 2 * T * H, "y")
+        s = _stream(stream)                     # after the tensor checks
         calls = []
         if stages == "path":
             calls.append((lib.moe_route_topk, (c, _ptr(logits, torch.float32, 4 * T * E, "logits"), ids, w, s),

@@ -235,3 +235,27 @@ def test_allgather_dispatch_validates_arguments(b):
                                         None, ctypes.byref(h1), None) == 0
     assert not h1.send_meta and b.lib.moe_combine(h0, ctypes.byref(h1), None, None, None, None, None) == 0
     b.lib.moe_ctx_destroy(h0)
+
+
+def test_prepared_path_checks_its_tensors_once_without_a_gpu(b):
+    # the prepared calls run the same checks as the individual functions at set-up:
+    # tensors that are not on the GPU, an unknown stage list, missing logits and the
+    # all-gather dispatcher's missing direct form are refused before any library call
+    import torch
+    ctx = b.Context(2, 4, 4, 2, 64)
+    T, E, k, H, Na = 8, 4, 2, 64, 16
+    bufs = {"topk_ids": torch.zeros(T, k, dtype=torch.int32), "topk_w": torch.zeros(T, k),
+            "workspace": torch.zeros(ctx.workspace_bytes, dtype=torch.uint8),
+            "send": torch.zeros(Na, 2 * H, dtype=torch.uint8), "recv": torch.zeros(Na, 2 * H, dtype=torch.uint8),
+            "send_scales": None, "recv_scales": None, "expert_out": torch.zeros(Na, H, dtype=torch.int16),
+            "comb": torch.zeros(Na, H, dtype=torch.int16), "y": torch.zeros(T, H, dtype=torch.int16)}
+    x = torch.zeros(T, H, dtype=torch.int16)
+    logits = torch.zeros(T, E)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b.PreparedPath(ctx, bufs, x, logits)
+    with pytest.raises(ValueError, match="stages"):
+        b.PreparedPath(ctx, bufs, x, logits, stages="combine")
+    with pytest.raises(ValueError, match="logits"):
+        b.PreparedPath(ctx, bufs, x, None)
+    with pytest.raises(ValueError, match="direct form"):
+        b.PreparedPath(ctx, bufs, x, None, direct=True, stages="dispatch_combine", gathered=torch.zeros(1))
