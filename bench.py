@@ -266,8 +266,14 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
                 break
     finally:
         os.sched_setaffinity(0, old)
+    flags = ""
+    with open(os.path.join(ROOT, "oracle", "Makefile")) as fh:     # how the timed oracle was compiled
+        for line in fh:
+            if line.startswith("CFLAGS"):
+                flags = line.split("=", 1)[1].strip()
     return {
         "value": reps * sh.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "build": f"{os.environ.get('CC', 'gcc')} {flags}",
         "sample": (f"{'whole workload' if tp == Tp else f'first {tp} of {Tp} tokens on each of {P} ranks'}"
                    f" ({sh.T} tokens), route+dispatch+stub+combine, {reps} passes in {el:.1f} s, "
                    f"single-threaded C oracle pinned to host core {core}"),

@@ -106,3 +106,12 @@ def test_counter_ingestion_scales_by_the_copy_calibration(tmp_path):
     rec = json.load(open(out))["cX"]["exchange"]
     assert rec["fetch_bytes"] == 2 * 200 * 1024 and rec["write_bytes"] == 400 * 1024
     assert rec["source_sha"] == bench.source_sha("exchange")
+
+
+def test_cpu_baseline_reports_its_sample_cores_and_build(orc):
+    import bench
+    from combine_router_softmax_expert_amd import workloads as wl
+    w = wl.WORKLOADS["c1"]
+    r = bench.cpu_baseline(w, wl.make_inputs(w), 0.2)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "tokens/s" and r["value"] > 0
+    assert "-ffp-contract=off" in r["build"] and "256 tokens" in r["sample"]
