@@ -85,11 +85,11 @@ __device__ __forceinline__ void st16(uint4* p, const uint4& v) {
 // (SC1): the line is written through the XCD's L2 to the device's coherence
 // point while the kernel runs, so no dirty lines are left for the write-back
 // at the kernel boundary, and the next kernel, whose workgroups read the row
-// from any XCD, finds it there.  Measured on gfx950 against write-back stores:
-// 128 tokens x top-8 x 7168 step 32.8-33.2 -> 31.7-32.0 us, 2048 tokens x
-// top-2 FP8 step 72.9 -> 69.4-69.8 us, and the pack of 8192 tokens x top-8
-// 93.8 -> 89.7 us.  The buffer's record count is the row's bytes, so the
-// hardware drops any store past the row.
+// from any XCD, finds it there.  Measured on gfx950 against write-back stores,
+// per step of the whole path: 128 tokens x top-8 x 7168, 32.3 -> 30.4 us;
+// 2048 tokens x top-2 FP8, 72.2 -> 68.6 us; and the pack of 8192 tokens x
+// top-8, 93.8 -> 89.8 us.  The buffer's record count is the row's bytes, so
+// the hardware drops any store past the row.
 constexpr int kRawBufferWord3 = 0x00020000;   // word 3 of a raw (untyped) gfx9 buffer resource
 constexpr int kStoreDeviceScope = 16;         // cache-policy operand: SC1
 
