@@ -156,7 +156,10 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
 
 template <int V>
 hipError_t launch_rtw(const Dims& d, const float* logits, int32_t* ids, float* w, hipStream_t st) {
-    constexpr int kThreads = 256;
+    // one wave (one token) per workgroup: at 128 tokens the tokens spread over 128
+    // compute units instead of 32 (step 30.6 -> 30.2 us measured on gfx950; no
+    // change at 8192 tokens)
+    constexpr int kThreads = kWave;
     const int tokens_per_block = kThreads / kWave;
     const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
     launch_kernel((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
