@@ -20,6 +20,7 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_STALE_HANDLE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_NO_MEMORY = -6
 
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_FP8_E4M3 = 1
@@ -91,7 +92,7 @@ lib = _load()
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         msg = lib.moe_status_string(status).decode()
-        extra = lib.moe_last_error().decode() if status == MOE_ERR_HIP else ""
+        extra = lib.moe_last_error().decode()   # the failing call's reason, "" if it gave none
         super().__init__(f"{where}: {msg}" + (f" ({extra})" if extra else ""))
         self.status = status
 

@@ -22,15 +22,25 @@ constexpr size_t kAlign = 256;
 constexpr int kFp8Block = 128;   // channels per FP8 scale, per token
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// A roctx range around one library call, so that a rocprofv3 --marker-trace
-// shows each call of the path (route, dispatch and its halves, stub, combine and
-// its halves) around the kernels it launched.
-struct CallRange {
-    explicit CallRange(const char* name) { roctxRangePushA(name); }
-    ~CallRange() { roctxRangePop(); }
-    CallRange(const CallRange&) = delete;
-    CallRange& operator=(const CallRange&) = delete;
+// Opens one library call: clears this thread's error text (so moe_last_error
+// always describes the latest call) and pushes a roctx range, so that a
+// rocprofv3 --marker-trace shows each call of the path (route, dispatch and its
+// halves, stub, combine and its halves) around the kernels it launched.
+struct CallScope {
+    explicit CallScope(const char* name) {
+        g_last_error.clear();
+        roctxRangePushA(name);
+    }
+    ~CallScope() { roctxRangePop(); }
+    CallScope(const CallScope&) = delete;
+    CallScope& operator=(const CallScope&) = delete;
 };
+
+// A failing status with its reason, for moe_last_error.
+moe_status fail(moe_status s, const char* why) {
+    g_last_error = why;
+    return s;
+}
 
 struct TimingRecord {
     const char* name;
@@ -179,8 +189,9 @@ moe_status count_and_scan(moe_ctx* ctx, const moe::Dims& d, const int32_t* topk_
 }
 
 moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
-    if (!h) return MOE_ERR_INVALID_ARG;
-    if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0) return MOE_ERR_STALE_HANDLE;
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0)
+        return fail(MOE_ERR_STALE_HANDLE, "the handle is not from this ctx's latest dispatch");
     return MOE_OK;
 }
 
@@ -207,6 +218,7 @@ const char* moe_status_string(moe_status s) {
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_STALE_HANDLE: return "stale or foreign dispatch handle";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_NO_MEMORY: return "host allocation failed";
     }
     return "unknown status";
 }
@@ -214,14 +226,17 @@ const char* moe_status_string(moe_status s) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
-    if (!out) return MOE_ERR_INVALID_ARG;
+    g_last_error.clear();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    if (!shape) return MOE_ERR_INVALID_ARG;
+    if (!shape) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
     const moe_shape s = *shape;
     if (s.num_ranks < 1 || s.tokens_per_rank < 0 || s.num_experts < 1 || s.top_k < 1 || s.hidden < 8 ||
         s.num_experts % s.num_ranks != 0 || s.top_k > s.num_experts || s.hidden % 8 != 0 ||
         (s.dispatch_dtype != MOE_DTYPE_BF16 && s.dispatch_dtype != MOE_DTYPE_FP8_E4M3))
-        return MOE_ERR_INVALID_ARG;
+        return fail(MOE_ERR_INVALID_ARG,
+                    "shape: needs num_ranks >= 1, tokens_per_rank >= 0, 1 <= top_k <= num_experts, num_experts a "
+                    "multiple of num_ranks, hidden a positive multiple of 8 and a known dispatch_dtype");
     const bool fp8 = s.dispatch_dtype == MOE_DTYPE_FP8_E4M3;
     const long long T = (long long)s.num_ranks * s.tokens_per_rank;
     const long long Na = T * s.top_k;
@@ -231,10 +246,10 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
         // a row kernel's grid is at most N_a + P rows of H/8 units rounded up to a
         // workgroup (< 512 more), in one dimension of fewer than 2^32 work-items
         (Na + s.num_ranks) * (s.hidden / 8 + 512) >= (1LL << 32))
-        return MOE_ERR_UNSUPPORTED;
+        return fail(MOE_ERR_UNSUPPORTED, "shape outside the supported limits of moe_ctx_create");
 
     moe_ctx* ctx = new (std::nothrow) moe_ctx();
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    if (!ctx) return fail(MOE_ERR_NO_MEMORY, "host allocation of the ctx failed");
     ctx->shape = s;
     moe::Dims& d = ctx->d;
     d.P = s.num_ranks;
@@ -309,10 +324,10 @@ int32_t moe_scales_per_row(const moe_ctx* ctx) { return ctx ? ctx->d.scales : 0;
 int64_t moe_num_assignments(const moe_ctx* ctx) { return ctx ? ctx->d.Na : 0; }
 
 moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
-    const CallRange range("moe_route_topk");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_route_topk");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     if (ctx->d.T == 0) return MOE_OK;
-    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids or topk_w is NULL");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const moe::Dims d = ctx->d;
     return launch(ctx, "route_topk", st, [&] { return moe::launch_route_topk(d, logits, topk_ids, topk_w, st); });
@@ -321,13 +336,15 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, 
 moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                              void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
                              moe_handle* handle, void* stream) {
-    const CallRange range("moe_dispatch_send");
-    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_dispatch_send");
+    if (!ctx || !handle) return fail(MOE_ERR_INVALID_ARG, "ctx or handle is NULL");
     const moe::Dims d = ctx->d;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
-    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf)) return MOE_ERR_INVALID_ARG;
-    if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or not 256-byte aligned");
+    if (workspace_bytes < ctx->ws_bytes) return fail(MOE_ERR_WORKSPACE, "workspace_bytes < moe_workspace_bytes(ctx)");
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf))
+        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w or send_buf is NULL");
+    if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -349,8 +366,8 @@ moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* top
 
 moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
                              void* recv_buf, float* recv_scales, void* stream) {
-    const CallRange range("moe_dispatch_recv");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_dispatch_recv");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_handle(ctx, handle);
     if (s != MOE_OK) return s;
     if (!handle->send_meta || ctx->received == ctx->generation) {
@@ -358,9 +375,9 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
         return MOE_ERR_INVALID_ARG;
     }
     const moe::Dims d = ctx->d;
-    if (d.T > 0 && (!send_buf || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (d.T > 0 && (!send_buf || !recv_buf)) return fail(MOE_ERR_INVALID_ARG, "send_buf or recv_buf is NULL");
     if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
-        return MOE_ERR_INVALID_ARG;
+        return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
     if (d.T > 0) {
         const moe::Workspace ws = carve(ctx, ctx->workspace);
         hipStream_t st = static_cast<hipStream_t>(stream);
@@ -377,12 +394,12 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
 moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                         void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
                         void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
-    const CallRange range("moe_dispatch");
-    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_dispatch");
+    if (!ctx || !handle) return fail(MOE_ERR_INVALID_ARG, "ctx or handle is NULL");
     const moe::Dims d = ctx->d;
     // every argument is checked before anything is enqueued
-    if (d.T > 0 && !recv_buf) return MOE_ERR_INVALID_ARG;
-    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    if (d.T > 0 && !recv_buf) return fail(MOE_ERR_INVALID_ARG, "recv_buf is NULL");
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
     moe_status s = moe_dispatch_send(ctx, x, topk_ids, topk_w, workspace, workspace_bytes, send_buf, send_scales,
                                      handle, stream);
     if (s != MOE_OK) return s;
@@ -392,13 +409,15 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
 moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                void* workspace, size_t workspace_bytes, void* recv_buf, float* recv_scales,
                                moe_handle* handle, void* stream) {
-    const CallRange range("moe_dispatch_direct");
-    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_dispatch_direct");
+    if (!ctx || !handle) return fail(MOE_ERR_INVALID_ARG, "ctx or handle is NULL");
     const moe::Dims d = ctx->d;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
-    if (d.T > 0 && (!x || !topk_ids || !topk_w || !recv_buf)) return MOE_ERR_INVALID_ARG;
-    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return MOE_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or not 256-byte aligned");
+    if (workspace_bytes < ctx->ws_bytes) return fail(MOE_ERR_WORKSPACE, "workspace_bytes < moe_workspace_bytes(ctx)");
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !recv_buf))
+        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w or recv_buf is NULL");
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -423,16 +442,19 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
 moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                                   void* workspace, size_t workspace_bytes, void* gathered, float* gathered_scales,
                                   void* recv_buf, float* recv_scales, moe_handle* handle, void* stream) {
-    const CallRange range("moe_dispatch_allgather");
-    if (!ctx || !handle) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_dispatch_allgather");
+    if (!ctx || !handle) return fail(MOE_ERR_INVALID_ARG, "ctx or handle is NULL");
     const moe::Dims d = ctx->d;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return MOE_ERR_INVALID_ARG;
-    if (workspace_bytes < ctx->ws_bytes) return MOE_ERR_WORKSPACE;
-    if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf)) return MOE_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or not 256-byte aligned");
+    if (workspace_bytes < ctx->ws_bytes) return fail(MOE_ERR_WORKSPACE, "workspace_bytes < moe_workspace_bytes(ctx)");
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf))
+        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w, gathered or recv_buf is NULL");
     if (d.fp8 ? (d.T > 0 && (!gathered_scales || !recv_scales)) : (gathered_scales || recv_scales))
-        return MOE_ERR_INVALID_ARG;
+        return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
     // the gathered rows (P * T of them, indexed in 32 bits) in one grid dimension of fewer than 2^32 work-items
-    if ((long long)d.P * d.T * (d.H / 8 + 512) >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+    if ((long long)d.P * d.T * (d.H / 8 + 512) >= (1LL << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "P * T gathered rows exceed one grid dimension");
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -459,13 +481,14 @@ moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t
 
 moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* recv_buf, const float* recv_scales,
                            uint16_t* expert_out, void* stream) {
-    const CallRange range("moe_expert_stub");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_expert_stub");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_received(ctx, handle, "moe_expert_stub");
     if (s != MOE_OK) return s;
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
-    if (!recv_buf || !expert_out || (d.fp8 ? !recv_scales : recv_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!recv_buf || !expert_out) return fail(MOE_ERR_INVALID_ARG, "recv_buf or expert_out is NULL");
+    if (d.fp8 ? !recv_scales : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
     const moe::Workspace ws = from_handle(handle);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool affine = affine_layout(ctx, handle);
@@ -475,13 +498,13 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
 
 moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                             uint16_t* comb_buf, void* stream) {
-    const CallRange range("moe_combine_send");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_combine_send");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_received(ctx, handle, "moe_combine_send");
     if (s != MOE_OK) return s;
     const moe::Dims d = ctx->d;
     if (d.T > 0) {
-        if (!expert_out || !comb_buf) return MOE_ERR_INVALID_ARG;
+        if (!expert_out || !comb_buf) return fail(MOE_ERR_INVALID_ARG, "expert_out or comb_buf is NULL");
         const moe::Workspace ws = from_handle(handle);
         hipStream_t st = static_cast<hipStream_t>(stream);
         s = launch(ctx, "reverse_exchange", st,
@@ -496,8 +519,8 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
 
 moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
                             uint16_t* y, void* stream) {
-    const CallRange range("moe_combine_recv");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_combine_recv");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_received(ctx, handle, "moe_combine_recv");
     if (s != MOE_OK) return s;
     if (ctx->combine_sent != handle->generation) {
@@ -506,7 +529,7 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
     }
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
-    if (!comb_buf || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    if (!comb_buf || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "comb_buf, topk_w or y is NULL");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool affine = affine_layout(ctx, handle);
     return launch(ctx, "reduce", st,
@@ -515,11 +538,12 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
 
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out, const float* topk_w,
                        uint16_t* comb_buf, uint16_t* y, void* stream) {
-    const CallRange range("moe_combine");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_combine");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_received(ctx, handle, "moe_combine");
     if (s != MOE_OK) return s;
-    if (ctx->d.T > 0 && (!expert_out || !topk_w || !comb_buf || !y)) return MOE_ERR_INVALID_ARG;
+    if (ctx->d.T > 0 && (!expert_out || !topk_w || !comb_buf || !y))
+        return fail(MOE_ERR_INVALID_ARG, "expert_out, topk_w, comb_buf or y is NULL");
     s = moe_combine_send(ctx, handle, expert_out, comb_buf, stream);
     if (s != MOE_OK) return s;
     return moe_combine_recv(ctx, handle, comb_buf, topk_w, y, stream);
@@ -527,13 +551,13 @@ moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* e
 
 moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                               const float* topk_w, uint16_t* y, void* stream) {
-    const CallRange range("moe_combine_direct");
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    const CallScope scope("moe_combine_direct");
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     moe_status s = check_received(ctx, handle, "moe_combine_direct");
     if (s != MOE_OK) return s;
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
-    if (!expert_out || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+    if (!expert_out || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "expert_out, topk_w or y is NULL");
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launch(ctx, "reduce_direct", st, [&] {
         return moe::launch_reduce(d, expert_out, handle->recv_pos, topk_w, y, true, affine_layout(ctx, handle), st);
@@ -541,13 +565,15 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
 }
 
 moe_status moe_timing_begin(moe_ctx* ctx) {
-    if (!ctx) return MOE_ERR_INVALID_ARG;
+    g_last_error.clear();
+    if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     ctx->timing = true;
     return MOE_OK;
 }
 
 moe_status moe_timing_end(moe_ctx* ctx, moe_kernel_time* out, int32_t max, int32_t* count) {
-    if (!ctx || !count || (max > 0 && !out)) return MOE_ERR_INVALID_ARG;
+    g_last_error.clear();
+    if (!ctx || !count || (max > 0 && !out)) return fail(MOE_ERR_INVALID_ARG, "ctx, count or out is NULL");
     ctx->timing = false;
     std::vector<moe_kernel_time> agg;
     moe_status status = MOE_OK;

@@ -52,7 +52,8 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = -2,   /* shape outside the supported limits below */
     MOE_ERR_WORKSPACE = -3,     /* workspace smaller than moe_workspace_bytes() */
     MOE_ERR_STALE_HANDLE = -4,  /* handle not from the latest moe_dispatch of this ctx */
-    MOE_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_NO_MEMORY = -6      /* a host allocation inside the library failed */
 } moe_status;
 
 typedef enum {
@@ -122,7 +123,8 @@ typedef struct {
 /* ---- context and sizes ---------------------------------------------------- */
 
 /* Validates the shape and creates a context.  Returns MOE_ERR_INVALID_ARG or
- * MOE_ERR_UNSUPPORTED (and *out = NULL) for shapes outside the limits. */
+ * MOE_ERR_UNSUPPORTED (and *out = NULL) for shapes outside the limits, and
+ * MOE_ERR_NO_MEMORY if the context cannot be allocated. */
 moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out);
 void moe_ctx_destroy(moe_ctx* ctx);
 
@@ -278,7 +280,11 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
 
 /* Static, human-readable text of a status code. */
 const char* moe_status_string(moe_status status);
-/* Text of the last HIP error this thread saw inside the library ("" if none). */
+/* The reason for the status of this thread's latest library call: the HIP
+ * error, the argument that failed its check, or the call that must come first.
+ * Each call that returns a moe_status clears it on entry, so it is "" after
+ * such a call succeeded.  The pointer stays valid until this thread's next call
+ * that returns a moe_status. */
 const char* moe_last_error(void);
 
 /* Per-kernel timing: between moe_timing_begin and moe_timing_end every kernel

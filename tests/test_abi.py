@@ -70,9 +70,45 @@ def test_ctx_sizes(b):
 
 
 def test_status_strings(b):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert b.lib.moe_status_string(code)
+    assert len({b.lib.moe_status_string(c) for c in range(-6, 1)}) == 7
     assert b.lib.moe_status_string(7) == b"unknown status"
+
+
+def test_last_error_names_the_latest_calls_reason(b):
+    """Each failing call leaves its own reason; every call clears the previous one."""
+    st, h = _create(b, dt=1)            # FP8 dispatch: scales are required
+    assert st == 0 and b.lib.moe_last_error() == b""
+    try:
+        fake = ctypes.c_void_p(1 << 20)
+        ws = b.lib.moe_workspace_bytes(h)
+        hd = b.MoeHandle()
+        assert b.lib.moe_dispatch(h, fake, fake, fake, fake, ws - 1, fake, fake, fake, fake, ctypes.byref(hd),
+                                  None) == -3
+        assert b"workspace_bytes" in b.lib.moe_last_error()
+        assert b.lib.moe_dispatch(h, fake, fake, fake, ctypes.c_void_p((1 << 20) + 8), ws, fake, fake, fake, fake,
+                                  ctypes.byref(hd), None) == -1
+        assert b"aligned" in b.lib.moe_last_error()
+        assert b.lib.moe_dispatch(h, fake, fake, fake, fake, ws, fake, None, fake, fake, ctypes.byref(hd),
+                                  None) == -1
+        assert b"scales" in b.lib.moe_last_error()
+        assert b.lib.moe_expert_stub(h, ctypes.byref(hd), fake, fake, fake, None) == -4
+        assert b"latest dispatch" in b.lib.moe_last_error()
+        assert b.lib.moe_route_topk(h, None, fake, fake, None) == -1
+        assert b"logits" in b.lib.moe_last_error()
+        assert b.lib.moe_timing_begin(h) == 0 and b.lib.moe_last_error() == b""   # cleared by a call that succeeds
+        n = ctypes.c_int32(-1)
+        assert b.lib.moe_timing_end(h, None, 0, ctypes.byref(n)) == 0 and b.lib.moe_last_error() == b""
+        bad = b.MoeShape(4, 16, 6, 2, 256, 0)                                       # E not a multiple of P
+        out = ctypes.c_void_p()
+        assert b.lib.moe_ctx_create(ctypes.byref(bad), ctypes.byref(out)) == -1 and not out.value
+        assert b"multiple of num_ranks" in b.lib.moe_last_error()
+        # the Python error carries the reason for any status
+        with pytest.raises(b.MoeError, match=r"invalid argument \(.*multiple of num_ranks"):
+            b._check(-1, "moe_ctx_create")
+    finally:
+        b.lib.moe_ctx_destroy(h)
 
 
 def test_null_arguments(b):
