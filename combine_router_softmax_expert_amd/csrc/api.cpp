@@ -8,6 +8,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
 #include <vector>
@@ -40,6 +41,21 @@ struct CallScope {
 moe_status fail(moe_status s, const char* why) {
     g_last_error = why;
     return s;
+}
+
+moe_status bad_scales() { return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16"); }
+
+// Row arrays are moved 16 bytes per lane; the 4-byte arrays are read a word at
+// a time, wave-uniform ones through the scalar cache, which drops the low two
+// address bits.  NULL passes (the null checks come first).
+moe_status check_alignment(std::initializer_list<const void*> rows, std::initializer_list<const void*> words) {
+    for (const void* p : rows)
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(MOE_ERR_INVALID_ARG, "a row buffer is not 16-byte aligned");
+    for (const void* p : words)
+        if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+            return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids, topk_w or a scale array is not 4-byte aligned");
+    return MOE_OK;
 }
 
 struct TimingRecord {
@@ -328,6 +344,7 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, 
     if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");
     if (ctx->d.T == 0) return MOE_OK;
     if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids or topk_w is NULL");
+    if (moe_status a = check_alignment({}, {logits, topk_ids, topk_w}); a != MOE_OK) return a;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const moe::Dims d = ctx->d;
     return launch(ctx, "route_topk", st, [&] { return moe::launch_route_topk(d, logits, topk_ids, topk_w, st); });
@@ -344,7 +361,8 @@ moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* top
     if (workspace_bytes < ctx->ws_bytes) return fail(MOE_ERR_WORKSPACE, "workspace_bytes < moe_workspace_bytes(ctx)");
     if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf))
         return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w or send_buf is NULL");
-    if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+    if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return bad_scales();
+    if (moe_status a = check_alignment({x, send_buf}, {topk_ids, topk_w, send_scales}); a != MOE_OK) return a;
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -377,7 +395,8 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
     const moe::Dims d = ctx->d;
     if (d.T > 0 && (!send_buf || !recv_buf)) return fail(MOE_ERR_INVALID_ARG, "send_buf or recv_buf is NULL");
     if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
-        return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+        return bad_scales();
+    if (moe_status a = check_alignment({send_buf, recv_buf}, {send_scales, recv_scales}); a != MOE_OK) return a;
     if (d.T > 0) {
         const moe::Workspace ws = carve(ctx, ctx->workspace);
         hipStream_t st = static_cast<hipStream_t>(stream);
@@ -399,7 +418,8 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
     const moe::Dims d = ctx->d;
     // every argument is checked before anything is enqueued
     if (d.T > 0 && !recv_buf) return fail(MOE_ERR_INVALID_ARG, "recv_buf is NULL");
-    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return bad_scales();
+    if (moe_status a = check_alignment({recv_buf}, {recv_scales}); a != MOE_OK) return a;
     moe_status s = moe_dispatch_send(ctx, x, topk_ids, topk_w, workspace, workspace_bytes, send_buf, send_scales,
                                      handle, stream);
     if (s != MOE_OK) return s;
@@ -417,7 +437,8 @@ moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* t
     if (workspace_bytes < ctx->ws_bytes) return fail(MOE_ERR_WORKSPACE, "workspace_bytes < moe_workspace_bytes(ctx)");
     if (d.T > 0 && (!x || !topk_ids || !topk_w || !recv_buf))
         return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w or recv_buf is NULL");
-    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+    if (d.fp8 ? (d.T > 0 && !recv_scales) : recv_scales != nullptr) return bad_scales();
+    if (moe_status a = check_alignment({x, recv_buf}, {topk_ids, topk_w, recv_scales}); a != MOE_OK) return a;
 
     const moe::Workspace ws = carve(ctx, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -451,7 +472,10 @@ moe_status moe_dispatch_allgather(moe_ctx* ctx, const uint16_t* x, const int32_t
     if (d.T > 0 && (!x || !topk_ids || !topk_w || !gathered || !recv_buf))
         return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w, gathered or recv_buf is NULL");
     if (d.fp8 ? (d.T > 0 && (!gathered_scales || !recv_scales)) : (gathered_scales || recv_scales))
-        return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+        return bad_scales();
+    if (moe_status a = check_alignment({x, gathered, recv_buf}, {topk_ids, topk_w, gathered_scales, recv_scales});
+        a != MOE_OK)
+        return a;
     // the gathered rows (P * T of them, indexed in 32 bits) in one grid dimension of fewer than 2^32 work-items
     if ((long long)d.P * d.T * (d.H / 8 + 512) >= (1LL << 32))
         return fail(MOE_ERR_UNSUPPORTED, "P * T gathered rows exceed one grid dimension");
@@ -488,7 +512,8 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
     if (!recv_buf || !expert_out) return fail(MOE_ERR_INVALID_ARG, "recv_buf or expert_out is NULL");
-    if (d.fp8 ? !recv_scales : recv_scales != nullptr) return fail(MOE_ERR_INVALID_ARG, "scales: required for FP8 dispatch, NULL for bf16");
+    if (d.fp8 ? !recv_scales : recv_scales != nullptr) return bad_scales();
+    if (moe_status a = check_alignment({recv_buf, expert_out}, {recv_scales}); a != MOE_OK) return a;
     const moe::Workspace ws = from_handle(handle);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool affine = affine_layout(ctx, handle);
@@ -505,6 +530,7 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
     const moe::Dims d = ctx->d;
     if (d.T > 0) {
         if (!expert_out || !comb_buf) return fail(MOE_ERR_INVALID_ARG, "expert_out or comb_buf is NULL");
+        if (moe_status a = check_alignment({expert_out, comb_buf}, {}); a != MOE_OK) return a;
         const moe::Workspace ws = from_handle(handle);
         hipStream_t st = static_cast<hipStream_t>(stream);
         s = launch(ctx, "reverse_exchange", st,
@@ -530,6 +556,7 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
     if (!comb_buf || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "comb_buf, topk_w or y is NULL");
+    if (moe_status a = check_alignment({comb_buf, y}, {topk_w}); a != MOE_OK) return a;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool affine = affine_layout(ctx, handle);
     return launch(ctx, "reduce", st,
@@ -544,6 +571,7 @@ moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* e
     if (s != MOE_OK) return s;
     if (ctx->d.T > 0 && (!expert_out || !topk_w || !comb_buf || !y))
         return fail(MOE_ERR_INVALID_ARG, "expert_out, topk_w, comb_buf or y is NULL");
+    if (moe_status a = check_alignment({expert_out, comb_buf, y}, {topk_w}); a != MOE_OK) return a;
     s = moe_combine_send(ctx, handle, expert_out, comb_buf, stream);
     if (s != MOE_OK) return s;
     return moe_combine_recv(ctx, handle, comb_buf, topk_w, y, stream);
@@ -558,6 +586,7 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
     const moe::Dims d = ctx->d;
     if (d.T == 0) return MOE_OK;
     if (!expert_out || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "expert_out, topk_w or y is NULL");
+    if (moe_status a = check_alignment({expert_out, y}, {topk_w}); a != MOE_OK) return a;
     hipStream_t st = static_cast<hipStream_t>(stream);
     return launch(ctx, "reduce_direct", st, [&] {
         return moe::launch_reduce(d, expert_out, handle->recv_pos, topk_w, y, true, affine_layout(ctx, handle), st);

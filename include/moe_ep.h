@@ -23,6 +23,11 @@
  *  - Every data pointer is a DEVICE pointer into caller-owned memory on the
  *    current HIP device; ctx, shape, handle and status outputs are HOST
  *    pointers.  `stream` is a hipStream_t (NULL = default stream).
+ *  - Alignment: row buffers (x, send_buf, recv_buf, gathered, expert_out,
+ *    comb_buf, y) start on 16 bytes, since kernels move rows 16 bytes per
+ *    lane; logits, topk_ids, topk_w and the scale arrays on 4 bytes.  Else
+ *    MOE_ERR_INVALID_ARG.  torch and hipMalloc allocations, and whole-row
+ *    slices of them, satisfy both.
  *  - Calls only enqueue work on `stream`: they never allocate device memory,
  *    never synchronise and never read device data on the host ([A2A] 3.5: a
  *    count read back to the CPU puts a hole before the exchange; [EP]

@@ -76,6 +76,32 @@ def test_status_strings(b):
     assert b.lib.moe_status_string(7) == b"unknown status"
 
 
+def test_misaligned_pointers_are_refused_before_any_launch(b):
+    """Row buffers need 16-byte alignment, the 4-byte arrays 4 bytes (CPU: every case fails before a launch)."""
+    st, h = _create(b, dt=1)
+    try:
+        a = 1 << 20
+        ok, row8, word2 = ctypes.c_void_p(a), ctypes.c_void_p(a + 8), ctypes.c_void_p(a + 2)
+        ws = b.lib.moe_workspace_bytes(h)
+        assert b.lib.moe_route_topk(h, word2, ok, ok, None) == -1
+        assert b"4-byte" in b.lib.moe_last_error()
+        hd = b.MoeHandle()
+        # moe_dispatch: x, topk_ids, topk_w, workspace, bytes, send, send_scales, recv, recv_scales
+        cases = [(row8, ok, ok, ok, ok, b"16-byte"), (ok, word2, ok, ok, ok, b"4-byte"),
+                 (ok, ok, row8, ok, ok, b"16-byte"), (ok, ok, ok, word2, ok, b"4-byte"),
+                 (ok, ok, ok, ok, row8, b"16-byte")]
+        for x, ids, send, send_sc, recv, why in cases:
+            assert b.lib.moe_dispatch(h, x, ids, ok, ok, ws, send, send_sc, recv, ok, ctypes.byref(hd), None) == -1
+            assert why in b.lib.moe_last_error()
+            assert hd.generation == 0                      # nothing was published
+        assert b.lib.moe_dispatch_direct(h, row8, ok, ok, ok, ws, ok, ok, ctypes.byref(hd), None) == -1
+        assert b.lib.moe_dispatch_allgather(h, ok, ok, ok, ok, ws, row8, ok, ok, ok, ctypes.byref(hd), None) == -1
+        assert b.lib.moe_dispatch_send(h, ok, ok, word2, ok, ws, ok, ok, ctypes.byref(hd), None) == -1
+        assert b"4-byte" in b.lib.moe_last_error() and hd.generation == 0
+    finally:
+        b.lib.moe_ctx_destroy(h)
+
+
 def test_last_error_names_the_latest_calls_reason(b):
     """Each failing call leaves its own reason; every call clears the previous one."""
     st, h = _create(b, dt=1)            # FP8 dispatch: scales are required

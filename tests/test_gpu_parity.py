@@ -307,6 +307,43 @@ def test_combine_identity_top1_expert0(orc):
     assert np.array_equal(g["y"], x)
 
 
+def test_misaligned_buffers_are_refused_after_a_dispatch(orc):
+    """With a live handle the stub and combine calls refuse byte-offset buffers
+    before launching anything; the path then completes with the oracle's y."""
+    import ctypes
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    w = wl.WORKLOADS["c1"]
+    inp = wl.make_inputs(w)
+    sh = orc.Shape.of(w)
+    ids, wt = orc.route(sh, inp["logits"])
+    log("[align] c1 base, given ids")
+    ctx = B.Context.for_workload(w)
+    bufs = ctx.allocate()
+    bufs["topk_ids"].copy_(torch.from_numpy(ids))
+    bufs["topk_w"].copy_(torch.from_numpy(wt))
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+    h = B.moe_dispatch(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"], None,
+                       bufs["recv"], None)
+
+    def at(key, off=0):
+        return ctypes.c_void_p(bufs[key].data_ptr() + off)
+
+    c, hp = ctx.handle_ptr, ctypes.byref(h)
+    assert B.lib.moe_expert_stub(c, hp, at("recv", 8), None, at("expert_out"), None) == -1
+    assert b"16-byte" in B.lib.moe_last_error()
+    assert B.lib.moe_combine(c, hp, at("expert_out"), at("topk_w", 2), at("comb"), at("y"), None) == -1
+    assert b"4-byte" in B.lib.moe_last_error()
+    assert B.lib.moe_combine_send(c, hp, at("expert_out"), at("comb", 8), None) == -1
+    assert B.lib.moe_combine_direct(c, hp, at("expert_out", 8), at("topk_w"), at("y"), None) == -1
+    B.moe_expert_stub(ctx, h, bufs["recv"], None, bufs["expert_out"])
+    B.moe_combine(ctx, h, bufs["expert_out"], bufs["topk_w"], bufs["comb"], bufs["y"])
+    torch.cuda.synchronize()
+    o = orc.run(sh, inp["x"], ids=ids, w=wt)
+    assert np.array_equal(bufs["y"].view(torch.int16).cpu().numpy().view(np.uint16), o["y"].view(np.uint16))
+
+
 def test_zero_tokens(orc):
     from combine_router_softmax_expert_amd import binding as B
     import torch
