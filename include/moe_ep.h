@@ -40,6 +40,9 @@
  *    (the one place the library synchronises) and return MOE_ERR_INVALID_ARG,
  *    with the count in moe_last_error(), before launching anything else.
  *  - T = 0 is a valid no-op.  No C++ exception crosses this ABI.
+ *  - Threads: a ctx holds host state (the handle generation, the phase of the
+ *    split calls, timing records), so calls on one ctx must not overlap.
+ *    Different ctxs may be used from different threads at once.
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H
