@@ -98,7 +98,7 @@ def test_workload_parity_separate_count(orc, monkeypatch, name, direct):
                  direct=direct)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_workload_parity_allgather(orc, name):
     # every rank gathers every token and picks its own assignments; same receive side
     w = wl.WORKLOADS[name]
