@@ -102,6 +102,34 @@ def test_misaligned_pointers_are_refused_before_any_launch(b):
         b.lib.moe_ctx_destroy(h)
 
 
+def test_last_error_is_per_thread(b):
+    """Each thread reads the reason of its own latest call, whatever another thread did meanwhile."""
+    import threading
+    st, h = _create(b)
+    assert st == 0
+    gate = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, fail):
+        fail()
+        gate.wait()          # both threads have failed their call before either reads
+        gate.wait()
+        seen[name] = b.lib.moe_last_error()
+
+    fake = ctypes.c_void_p(1 << 20)
+    t1 = threading.Thread(target=worker, args=("route", lambda: b.lib.moe_route_topk(h, None, fake, fake, None)))
+    t2 = threading.Thread(target=worker, args=("ws", lambda: b.lib.moe_dispatch(
+        h, fake, fake, fake, fake, 0, fake, None, fake, None, ctypes.byref(b.MoeHandle()), None)))
+    try:
+        t1.start()
+        t2.start()
+        t1.join(30)
+        t2.join(30)
+        assert b"logits" in seen["route"] and b"workspace_bytes" in seen["ws"]
+    finally:
+        b.lib.moe_ctx_destroy(h)
+
+
 def test_last_error_names_the_latest_calls_reason(b):
     """Each failing call leaves its own reason; every call clears the previous one."""
     st, h = _create(b, dt=1)            # FP8 dispatch: scales are required

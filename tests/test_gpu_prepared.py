@@ -20,7 +20,8 @@ def _snapshot(bufs, direct):
     return {key: bufs[key].view(torch.uint8).clone() for key in keys}   # raw bytes: bit-exact comparison
 
 
-@pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True), ("c3", False)])
+@pytest.mark.parametrize("name,direct", [("c1", False), ("c1", True), ("c2", False), ("c2", True), ("c3", False),
+                                         ("c3", True)])
 def test_prepared_path_matches_run_path(name, direct):
     import torch
     from combine_router_softmax_expert_amd import binding as B
