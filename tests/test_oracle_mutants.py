@@ -34,6 +34,11 @@ MUTANTS = [
      "memcpy(o->recv_rows + p * rb, o->send_rows + q * rb, (size_t)rb);"),
     ("weight_from_wrong_slot", "m.weight = w[t * k + j];", "m.weight = w[t * k + (k - 1 - j)];"),
     ("count_matrix_transposed", "o->C[src * P + dst] = c;", "o->C[dst * P + src] = c;"),
+    ("stub_dequantises_with_block0_scale", "d = qv * scales[h / FP8_BLOCK];", "d = qv * scales[0];"),
+    ("amax_always_from_block0",
+     "for (int64_t h = b * FP8_BLOCK; h < (b + 1) * FP8_BLOCK; ++h) {\n            float a = fabsf",
+     "for (int64_t h = 0; h < FP8_BLOCK; ++h) {\n            float a = fabsf"),
+    ("stub_uses_local_expert", "oracle_stub_row(s, e, recv_rows", "oracle_stub_row(s, e % (s->E / s->P), recv_rows"),
 ]
 
 CHILD = r"""
