@@ -391,6 +391,7 @@ class PreparedPath:
         rb, nb = ctx.row_bytes, ctx.scales_per_row
         bf16 = (torch.bfloat16, torch.int16)
         self._keep = (ctx, bufs, x, logits, stream, gathered, gathered_scales)
+        self._ctx = ctx
         self.handle = MoeHandle()
         h = ctypes.byref(self.handle)
         c = ctx.handle_ptr
@@ -431,6 +432,8 @@ class PreparedPath:
         self._calls = tuple(calls)
 
     def __call__(self) -> MoeHandle:
+        if not self._ctx.handle_ptr:           # the cached calls hold the ctx pointer close() freed
+            raise ValueError("PreparedPath: its Context has been closed")
         for fn, args, name in self._calls:
             status = fn(*args)
             if status != MOE_OK:

@@ -327,6 +327,17 @@ def test_allgather_dispatch_validates_arguments(b):
     b.lib.moe_ctx_destroy(h0)
 
 
+def test_prepared_path_refuses_a_closed_context(b):
+    # the cached calls hold the ctx pointer; after close() they must not reach the library
+    ctx = b.Context(2, 4, 4, 2, 64)
+    path = b.PreparedPath.__new__(b.PreparedPath)
+    path._ctx, path._calls, path.handle = ctx, [(b.lib.moe_timing_begin, (ctx.handle_ptr,), "moe_timing_begin")], None
+    path()                                         # open: the cached call runs
+    ctx.close()
+    with pytest.raises(ValueError, match="closed"):
+        path()
+
+
 def test_prepared_path_checks_its_tensors_once_without_a_gpu(b):
     # the prepared calls run the same checks as the individual functions at set-up:
     # tensors that are not on the GPU, an unknown stage list, missing logits and the

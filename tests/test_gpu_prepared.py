@@ -56,6 +56,10 @@ def test_prepared_path_matches_run_path(name, direct):
         dc()
         torch.cuda.synchronize()
         assert torch.equal(bufs["y"].view(torch.uint8), want["y"]), (name, direct, i, "dispatch_combine")
+    torch.cuda.synchronize()
+    ctx.close()                          # the cached ctx pointer is gone: no call may reach the library
+    with pytest.raises(ValueError, match="closed"):
+        path()
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
