@@ -211,6 +211,7 @@ EDGE = [
 
 @pytest.mark.parametrize("policy,count,direct,layout", [("auto", "auto", False, "auto"),
                                                         ("streaming", "auto", False, "auto"),
+                                                        ("streaming", "auto", True, "auto"),
                                                         ("auto", "auto", True, "auto"),
                                                         ("auto", "separate", False, "auto"),
                                                         ("auto", "fused", True, "auto"),
