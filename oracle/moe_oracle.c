@@ -135,7 +135,12 @@ int64_t oracle_meta_bytes(void) { return (int64_t)sizeof(oracle_meta); }
 
 /* Slot order: slot 0 is the most probable expert.  Because softmax is strictly
  * increasing, ordering by probability is ordering by logit; equal logits are
- * broken towards the lower expert id. */
+ * broken towards the lower expert id.  A NaN logit has no place in that order
+ * and ranks below every number, -inf included (NaN against NaN is a tie, so
+ * the lower id again comes first); the weights of a row that holds a NaN are
+ * all NaN, because the softmax normaliser of that row is NaN. */
+static int ranks_before(float a, float b) { return !isnan(a) && (isnan(b) || a > b); }
+
 void oracle_route(const oracle_shape* s, const float* logits, int32_t* ids, float* w)
 {
     int64_t E = s->E, k = s->k;
@@ -154,7 +159,7 @@ void oracle_route(const oracle_shape* s, const float* logits, int32_t* ids, floa
             int64_t best = -1;
             for (int64_t e = 0; e < E; ++e) {
                 if (taken[e]) continue;
-                if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep the lower id */
+                if (best < 0 || ranks_before(l[e], l[best])) best = e;   /* strict: ties keep the lower id */
             }
             taken[best] = 1;
             ids[t * k + j] = (int32_t)best;

@@ -14,7 +14,9 @@ from conftest import ROOT
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 MUTANTS = [
-    ("ties_to_higher_id", "if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
+    ("ties_to_higher_id", "return !isnan(a) && (isnan(b) || a > b);", "return !isnan(a) && (isnan(b) || a >= b);"),
+    ("nan_ranks_first", "return !isnan(a) && (isnan(b) || a > b);", "return isnan(a) ? !isnan(b) : (!isnan(b) && a > b);"),
+    ("nan_compares_as_is", "return !isnan(a) && (isnan(b) || a > b);", "return a > b;"),
     ("no_renormalisation", "w[t * k + j] = (float)(p[ids[t * k + j]] / sel);", "w[t * k + j] = (float)(p[ids[t * k + j]]);"),
     ("send_offsets_not_rank_based", "int32_t acc = (int32_t)(src * Tp * k);", "int32_t acc = 0;"),
     ("unstable_bucket_order", "int32_t c = cur[src * E + e]++;", "int32_t c = o->n[src * E + e] - 1 - cur[src * E + e]++;"),
@@ -55,6 +57,7 @@ pins = [
     ("brute_positions", lambda: tp.test_positions_brute_force_random(orc, 3, 5, 6, 3)),
     ("route_ties", lambda: tp.test_route_selection_brute_force_with_ties(orc)),
     ("route_weights", lambda: tp.test_route_weights_special_cases(orc)),
+    ("route_nan", lambda: tp.test_route_nan_logits_rank_last(orc)),
     ("identity", lambda: tp.test_combine_of_dispatch_is_identity_for_top1_expert0(orc)),
     ("slot_order", lambda: tp.test_reduce_slot_order_closed_form(orc)),
     ("stub_bf16", lambda: tp.test_stub_closed_form_bf16(orc)),

@@ -226,6 +226,33 @@ def test_route_selection_brute_force_with_ties(orc):
                 assert ids[t].tolist() == sel.tolist()
 
 
+def test_route_nan_logits_rank_last(orc):
+    """NaN logits rank below every number, -inf included, and tie with each other (lower
+    id first); a row that holds a NaN has NaN weights.  Checked against a sort of every row
+    by the key (is NaN, -logit, id), on rows with NaN in every position pattern: none, one
+    at the front, several, all."""
+    rng = np.random.default_rng(17)
+    for E in (3, 8, 40):
+        T = 96
+        logits = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+        logits[rng.random((T, E)) < 0.2] = np.nan
+        logits[rng.random((T, E)) < 0.1] = -np.inf
+        logits[0] = np.nan                       # a whole row of NaN
+        logits[1, 0] = np.nan                    # NaN before every number
+        logits[2] = -np.inf
+        logits[2, E - 1] = np.nan                # NaN after a row of -inf
+        logits[3] = np.arange(E, dtype=np.float32)   # no NaN at all
+        for k in sorted({1, 2, min(E, 8), E}):
+            ids, w = orc.route(orc.Shape(1, T, E, k, 8, False), logits)
+            for t in range(T):
+                order = sorted(range(E), key=lambda e: (bool(np.isnan(logits[t, e])),
+                                                        0.0 if np.isnan(logits[t, e]) else -float(logits[t, e]), e))
+                assert ids[t].tolist() == order[:k], (E, k, t)
+                if np.isnan(logits[t]).any():
+                    assert np.isnan(w[t]).all(), (E, k, t)
+            assert np.isfinite(w[3]).all()
+
+
 def test_route_weights_special_cases(orc):
     rng = np.random.default_rng(6)
     T, E = 256, 16
