@@ -441,6 +441,18 @@ class PreparedPath:
         return self.handle
 
 
+def _capturing(streams) -> bool:
+    """Whether the current stream, or any of ``streams``, is capturing a graph."""
+    import torch
+    if torch.cuda.is_current_stream_capturing():
+        return True
+    for st in streams:
+        with torch.cuda.stream(st):
+            if torch.cuda.is_current_stream_capturing():
+                return True
+    return False
+
+
 def run_overlapped(parts, comm_stream, compute_stream):
     """Micro-batches through the split phases on two streams.
 
@@ -450,8 +462,16 @@ def run_overlapped(parts, comm_stream, compute_stream):
     micro-batch's stages, so the expert stage of micro-batch i can overlap the
     dispatch of i+1 and the combine of i-1 ([PPLX]: send and receive halves let
     other work run in between).  Only launches and events: the caller
-    synchronises before reading the outputs.  Returns the handles."""
+    synchronises before reading the outputs.  Returns the handles.
+
+    Refuses graph capture (RuntimeError, before anything is enqueued): the schedule
+    records and waits on events it creates per call and drops when it returns, and
+    it does not fork from or join back into a capturing origin stream, which a
+    multi-stream capture needs."""
     import torch
+    if _capturing((comm_stream, compute_stream)):
+        raise RuntimeError("run_overlapped: a stream is capturing a graph; the two-stream schedule is not built "
+                           "for capture (its events live for one call and it does not join the capturing stream)")
     handles, dispatched, computed = [], [], []
     for ctx, bufs, x, logits in parts:
         moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"], comm_stream)

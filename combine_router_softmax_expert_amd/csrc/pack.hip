@@ -144,14 +144,16 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
             // exact remainder x - q0 * scale (an FMA).  The corrected quotient can be one
             // ulp off the correctly rounded one, but never across an E4M3 rounding
             // boundary: checked for every bf16 amax >= 2^-64 and every bf16 |x| <= amax
-            // (the remainder stays far from underflow there).  Three operations per
-            // channel instead of a full division.
+            // (the remainder stays far from underflow there).  The sign is copied from
+            // x: for x = -0 the correction adds +0 to -0 and would give +0, where the
+            // quotient -0 / scale is -0 (code 0x80); every other quotient already has
+            // the sign of x.  Four operations per channel instead of a full division.
             const float r = 1.0f / scale;
             float v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float q0 = f[i] * r;
-                v[i] = fmaf(fmaf(-q0, scale, f[i]), r, q0);
+                v[i] = __builtin_copysignf(fmaf(fmaf(-q0, scale, f[i]), r, q0), f[i]);
             }
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) q[w4] = pack4_e4m3(v[4 * w4], v[4 * w4 + 1], v[4 * w4 + 2], v[4 * w4 + 3]);

@@ -11,11 +11,15 @@
 // wave maximum with DPP row operations (pairs, quads, half rows, rows, then
 // row broadcasts; a few cycles each, no LDS traffic), then a ballot per slot v
 // finds the lowest expert id holding that value, so equal logits pick the lower
-// id; the winner is replaced by NaN, which the IEEE maximum ignores.
+// id; the winner is replaced by NaN, which the IEEE maximum ignores.  NaN logits
+// rank below every number (-inf included) and tie with each other: a round
+// whose maximum is NaN has only NaN logits left and takes the lowest id among
+// the experts not yet chosen.
 // E <= 32: a group of G lanes (the next power of two >= E) owns a token, 64/G
 // tokens per wave, and each round is a group arg-max over 64-bit keys
-// (order-preserving logit bits, then the complemented expert id) by
-// xor-butterfly shuffles.
+// (order-preserving logit bits, with every NaN mapped below -inf, then the
+// complemented expert id) by xor-butterfly shuffles.
+// A row that holds a NaN logit gets NaN weights: its softmax normaliser is NaN.
 // Softmax is strictly increasing, so selecting by logit is selecting by
 // probability, and the renormalised weight p_j / sum_sel p equals
 // exp(l_j - l_max) / sum_sel exp(l_i - l_max): the full partition function
@@ -28,8 +32,12 @@
 namespace moe {
 namespace {
 
+// Order-preserving key of a logit: -0 ranks equal to +0, every NaN ranks below
+// -inf (whose key is 0x007FFFFF) and above the 0 that marks an expert taken or
+// absent.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
-    uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 ranks equal to +0
+    if (f != f) return 0u;
+    uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
@@ -50,12 +58,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
     uint64_t key[V];
     const float* row = logits + (size_t)(valid ? t : 0) * E;
+    int nan_seen = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int e = gl + G * v;
         key[v] = 0;   // below every real key
-        if (valid && e < E) key[v] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)~(uint32_t)e;
+        if (valid && e < E) {
+            const float l = row[e];
+            nan_seen |= l != l;
+            key[v] = ((uint64_t)ordered_bits(l) << 32) | (uint32_t)~(uint32_t)e;
+        }
     }
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) nan_seen |= __shfl_xor(nan_seen, off, G);
 
     double my_l = 0.0;
     int my_id = 0;
@@ -82,7 +97,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     for (int j = 0; j < k; ++j) sum += __shfl(my_e, j, G);
     if (valid && gl < k) {
         ids[(size_t)t * k + gl] = my_id;
-        w[(size_t)t * k + gl] = (float)(my_e / sum);
+        w[(size_t)t * k + gl] = nan_seen ? __int_as_float(0x7FC00000) : (float)(my_e / sum);
     }
 }
 
@@ -119,12 +134,17 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
     if (t >= T) return;                  // whole waves leave together
     const float nan = __int_as_float(0x7FC00000);
     float val[V];
+    unsigned open = 0;                   // bit v: expert lane + 64 v exists and is not chosen yet
+    bool nan_here = false;
     const float* row = logits + (size_t)t * E;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int e = lane + kWave * v;
         val[v] = e < E ? row[e] : nan;
+        if (e < E) open |= 1u << v;
+        nan_here |= e < E && val[v] != val[v];
     }
+    const bool row_nan = __ballot(nan_here) != 0;   // the same in every lane
     float my_l = 0.0f;
     int my_id = 0;
     for (int j = 0; j < k; ++j) {
@@ -133,14 +153,25 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
         for (int v = 1; v < V; ++v) lm = fmaxf(lm, val[v]);
         const float M = wave_max(lm);
         int id = -1;                     // the lowest expert id holding M
+        if (M == M) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const unsigned long long hit = __ballot(val[v] == M);
-            if (id < 0 && hit) id = kWave * v + __ffsll((long long)hit) - 1;
+            for (int v = 0; v < V; ++v) {
+                const unsigned long long hit = __ballot(val[v] == M);
+                if (id < 0 && hit) id = kWave * v + __ffsll((long long)hit) - 1;
+            }
+        } else {                         // only NaN logits are left: the lowest id not chosen yet
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const unsigned long long hit = __ballot((open >> v) & 1u);
+                if (id < 0 && hit) id = kWave * v + __ffsll((long long)hit) - 1;
+            }
         }
 #pragma unroll
         for (int v = 0; v < V; ++v)
-            if (lane + kWave * v == id) val[v] = nan;
+            if (lane + kWave * v == id) {
+                val[v] = nan;
+                open &= ~(1u << v);
+            }
         if (lane == j) { my_id = id; my_l = M; }
     }
     // the k exponentials at once (lanes < k), then their sum in slot order
@@ -150,7 +181,7 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
     for (int j = 0; j < k; ++j) sum += readlane_f64(my_e, j);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
-        w[(size_t)t * k + lane] = (float)(my_e / sum);
+        w[(size_t)t * k + lane] = row_nan ? nan : (float)(my_e / sum);
     }
 }
 

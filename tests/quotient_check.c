@@ -1,14 +1,16 @@
 /* Exhaustive check of the FP8 quantiser's quotient (CPU, plain C).
  *
  * The pack kernel computes x / scale, with scale = RN(amax / 448) per
- * 128-channel block, as q1 = fma(fma(-q0, scale, x), r, q0) with
+ * 128-channel block, as q1 = copysign(fma(fma(-q0, scale, x), r, q0), x) with
  * q0 = RN(x * r) and r = RN(1 / scale) when amax >= 2^-64, and then encodes q1
  * as OCP E4M3 with round-to-nearest-even and saturation.  The method's
  * definition encodes RN(x / scale) instead.  This program walks every positive
  * finite bf16 amax in [lo_bits, hi_bits) and every bf16 x with 0 <= x <= amax
- * (the encoding and both quotients are odd in x, so negative x follow) and
- * counts the pairs whose E4M3 codes differ.  The encoder here is written from
- * the format: bias 7, 3 significand bits, subnormal step 2^-9, largest 448.
+ * and counts the pairs whose E4M3 codes differ.  For x != 0 the encoding and
+ * both quotients are odd in x (RN and fma are odd), so negative x follow; at
+ * x = -0 the fma's +0 + -0 = +0 breaks that, so both zeros are checked for
+ * every amax, bit for bit.  The encoder here is written from the format:
+ * bias 7, 3 significand bits, subnormal step 2^-9, largest 448.
  *
  * usage: quotient_check LO_BITS HI_BITS   -> prints "checked N mismatches M"
  */
@@ -61,9 +63,17 @@ int main(int argc, char** argv) {
             const float x = from_bf16((uint16_t)xb);
             const float q = x / scale;
             const float q0 = x * r;
-            const float q1 = fmaf(fmaf(-q0, scale, x), r, q0);
+            const float q1 = copysignf(fmaf(fmaf(-q0, scale, x), r, q0), x);
             ++checked;
             if (bits_of(q1) != bits_of(q) && e4m3_code(q1) != e4m3_code(q)) ++mismatches;
+        }
+        for (int zb = 0; zb < 2; ++zb) {            /* +0 and -0: the sign decides the code */
+            const float x = from_bf16((uint16_t)(zb ? 0x8000 : 0x0000));
+            const float q = x / scale;
+            const float q0 = x * r;
+            const float q1 = copysignf(fmaf(fmaf(-q0, scale, x), r, q0), x);
+            ++checked;
+            if (bits_of(q1) != bits_of(q)) ++mismatches;
         }
     }
     printf("checked %lld mismatches %lld\n", checked, mismatches);

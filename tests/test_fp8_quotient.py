@@ -48,7 +48,17 @@ def test_corrected_reciprocal_quotient_gives_the_same_e4m3_codes(tmp_path):
 
 
 def test_check_catches_an_uncorrected_reciprocal(tmp_path):
-    text = open(SRC).read().replace("const float q1 = fmaf(fmaf(-q0, scale, x), r, q0);", "const float q1 = q0;")
+    text = open(SRC).read().replace("const float q1 = copysignf(fmaf(fmaf(-q0, scale, x), r, q0), x);",
+                                    "const float q1 = q0;")
     assert "q1 = q0;" in text
     checked, mismatches = _run(_build(tmp_path, text, "uncorrected"), lo=0x3F00, hi=0x4000, parts=4)
     assert mismatches > 0
+
+
+def test_check_catches_the_lost_sign_of_minus_zero(tmp_path):
+    # without the sign copy the correction turns -0 into +0: code 0x00 where the quotient gives 0x80
+    text = open(SRC).read().replace("const float q1 = copysignf(fmaf(fmaf(-q0, scale, x), r, q0), x);",
+                                    "const float q1 = fmaf(fmaf(-q0, scale, x), r, q0);")
+    assert text.count("const float q1 = fmaf(") == 2
+    checked, mismatches = _run(_build(tmp_path, text, "unsigned_zero"), lo=0x3F00, hi=0x3F10, parts=2)
+    assert mismatches == 16          # -0 under each of the 16 amax values of the range, nothing else

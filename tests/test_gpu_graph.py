@@ -1,15 +1,19 @@
 """The whole path captured in a HIP graph (torch.cuda.CUDAGraph on the caller's
-stream) and replayed: every replay must reproduce, bit for bit, what the eager
-calls produce on the same inputs, with new inputs copied into the captured
-buffers and eager work and synchronisations between replays.  The library only
-enqueues kernel launches on the caller's stream (no allocation, no memset, no
-host synchronisation), which is what makes the capture valid."""
+stream) and replayed ([A2A] 9: a low-latency decode path keeps host work and
+synchronisation off the step).  With new inputs copied into the captured buffers,
+the outputs poisoned before each replay and eager work and synchronisations
+between replays, every replay must give the oracle's outputs for its inputs
+(ids, integer parts, rows, scales, expert outputs and combine rows bit for bit,
+weights and y to the parity tolerances) and, bit for bit, what eager calls give
+on the same inputs.  The library only enqueues kernel launches on the caller's
+stream (no allocation, no memset, no host synchronisation), which is what makes
+the capture valid."""
 
 import numpy as np
 import pytest
 
 from combine_router_softmax_expert_amd import workloads as wl
-from gpu_helpers import log
+from gpu_helpers import compare_with_oracle, log, oracle_path, read_back
 
 pytestmark = pytest.mark.gpu
 
@@ -23,18 +27,20 @@ def _snapshot(bufs, direct):
 
 
 @pytest.mark.parametrize("name,direct", [("c1", False), ("c2", False), ("c2", True), ("c3", True)])
-def test_graph_replays_match_eager_calls(name, direct):
+def test_graph_replays_match_the_oracle(orc, name, direct):
     import torch
     from combine_router_softmax_expert_amd import binding as B
 
     log(f"[graph] {name} direct={direct}")
     w = wl.WORKLOADS[name]
+    sh = orc.Shape.of(w)
     ctx = B.Context.for_workload(w)
     bufs = ctx.allocate()
     inputs = [wl.make_inputs(w)]
     for seed in (11, 12, 13):     # three more input sets of the same shape for the replays
         inputs.append({"x": wl.make_hidden(seed, w.tokens, w.hidden), "logits": wl.make_logits(seed, w.tokens,
                                                                                               w.num_experts)})
+    oracle = [oracle_path(orc, sh, i["x"], logits=i["logits"]) for i in inputs]
     xs = [torch.from_numpy(i["x"].view(np.int16)).cuda() for i in inputs]
     ls = [torch.from_numpy(i["logits"]).cuda() for i in inputs]
     x = xs[0].clone()
@@ -58,7 +64,7 @@ def test_graph_replays_match_eager_calls(name, direct):
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        B.run_path(ctx, bufs, x, logits, direct=direct)
+        h = B.run_path(ctx, bufs, x, logits, direct=direct)   # the handle's arrays: fixed workspace addresses
     torch.cuda.synchronize()
 
     for rep in range(2):
@@ -74,4 +80,6 @@ def test_graph_replays_match_eager_calls(name, direct):
             got = _snapshot(bufs, direct)
             for key, want in expected[i].items():
                 assert torch.equal(got[key], want), (name, direct, rep, i, key)
+            g = read_back(sh, ctx, bufs, h, direct=direct)
+            compare_with_oracle(orc, sh, g, inputs[i]["x"], logits=inputs[i]["logits"], o=oracle[i])
             del scratch

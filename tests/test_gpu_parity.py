@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 from combine_router_softmax_expert_amd import workloads as wl
-from gpu_helpers import (assert_integer_parts_equal, assert_weights_close, assert_y_close, bf16_to_f32, log,
-                         run_gpu)
+from gpu_helpers import (INT_KEYS, assert_bf16_equal, assert_integer_parts_equal, assert_weights_close, assert_y_close,
+                         bf16_to_f32, compare_with_oracle, log, record_weights_match, run_gpu, weights_equal)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,28 +20,8 @@ pytestmark = pytest.mark.gpu
 def _full_parity(orc, sh, x, logits=None, ids=None, w=None, label="", direct=False, allgather=False):
     log(f"[parity] {label} P={sh.P} T={sh.T} E={sh.E} k={sh.k} H={sh.H} fp8={sh.fp8} "
         f"{'route' if ids is None else 'given ids'}{' direct' if direct else ''}")
-    if ids is None:
-        o_ids, o_w = orc.route(sh, logits)
-    else:
-        o_ids, o_w = ids, w
     g = run_gpu(sh, x, logits=logits, ids=ids, w=w, direct=direct, allgather=allgather)
-    assert np.array_equal(g["ids"], o_ids)
-    if ids is None:
-        assert_weights_close(g["w"], o_w)
-    else:
-        assert np.array_equal(g["w"], o_w)
-    o = orc.run(sh, x, ids=o_ids, w=o_w)
-    assert_integer_parts_equal(g, o)
-    for key in ("send_rows", "recv_rows", "send_scales", "recv_scales", "expert_out", "comb"):
-        if o[key] is None or g[key] is None:
-            continue
-        assert np.array_equal(g[key].view(np.uint8), o[key].view(np.uint8)), key
-    assert np.array_equal(g["recv_meta"]["weight"], g["w"].ravel()[np.argsort(g["recv_pos"].ravel())])
-    if g["send_meta"] is not None:
-        assert np.array_equal(g["send_meta"]["weight"], g["w"].ravel()[np.argsort(g["send_pos"].ravel())])
-    assert_y_close(g["y"], o["y32"])
-    if np.array_equal(g["w"], o_w):
-        assert np.array_equal(g["y"], o["y"])
+    o = compare_with_oracle(orc, sh, g, x, logits=logits, ids=ids, w=w)
     if allgather:
         # every rank's copy holds every token in its dispatched form
         if sh.fp8:
@@ -124,49 +104,52 @@ def test_workload_parity_with_oracle_routing(orc):
     assert np.array_equal(g["y"], o["y"])
 
 
-@pytest.mark.parametrize("mode", ["base", "direct", "allgather"])
-def test_skewed_workload_full_size_sampled(orc, mode):
-    # c5 at its full size, in the launch configuration the benchmark times: all
-    # routing, counts, offsets, positions and handle records in full; payload,
-    # stub and combine on sampled tokens that the oracle computes one by one
+@pytest.fixture(scope="module")
+def skewed_oracle(orc):
+    """c5 at its full size through the whole oracle path, once for the three forms below."""
     w = wl.WORKLOADS["c5"]
     sh = orc.Shape.of(w)
-    direct, allgather = mode == "direct", mode == "allgather"
-    log(f"[parity] c5 full size {mode}, generating inputs")
+    log("[parity] c5 full size: inputs and the oracle's whole path")
     inp = wl.make_inputs(w)
-    o_ids, o_w = orc.route(sh, inp["logits"])
+    ids, wt = orc.route(sh, inp["logits"])
+    o = orc.run(sh, inp["x"], ids=ids, w=wt)
+    return w, sh, inp, o
+
+
+@pytest.mark.parametrize("mode", ["base", "direct", "allgather"])
+def test_skewed_workload_full_parity(skewed_oracle, mode):
+    """c5 (32 ranks, 8192 tokens, E=256, top-8, H=7168, FP8, Zipf-skewed routing) at its full size, in
+    the launch configuration the benchmark times, element by element against the oracle: every
+    routing id and weight, count, offset, position and handle record, every send and receive row
+    with its scales, every expert output and combine row, every y, and in the all-gather form every
+    rank's copy of every token."""
+    w, sh, inp, o = skewed_oracle
+    direct, allgather = mode == "direct", mode == "allgather"
+    log(f"[parity] c5 full size {mode}")
     g = run_gpu(sh, inp["x"], logits=inp["logits"], direct=direct, allgather=allgather)
-    assert np.array_equal(g["ids"], o_ids)
-    assert_weights_close(g["w"], o_w)
-    o = orc.dispatch(sh, inp["x"], o_ids, o_w, payload=False)
+    assert np.array_equal(g["ids"], o["ids"])
+    assert_weights_close(g["w"], o["w"])
     assert_integer_parts_equal(g, o)
     n = np.sort(o["N"])[::-1]
     assert 0.40 <= n[: w.num_experts // 10].sum() / n.sum() <= 0.50
-    rng = np.random.default_rng(5)
-    tokens = np.unique(np.concatenate([[0, sh.T - 1], rng.integers(0, sh.T, 48)]))
-    nb = sh.H // 128
-    stub_rows = np.empty((len(tokens), sh.k, sh.H), np.uint16)
-    for r, t in enumerate(tokens):
-        q, sc = orc.quantize_row(sh.H, inp["x"][t])
-        for j in range(sh.k):
-            p, qq = o["send_pos"][t, j], o["recv_pos"][t, j]
-            assert np.array_equal(g["recv_rows"][qq], q) and np.array_equal(g["recv_scales"][qq], sc)
-            if mode == "base":
-                assert np.array_equal(g["send_rows"][p], q) and np.array_equal(g["send_scales"][p], sc)
-            if allgather:               # the token in every rank's copy
-                for rr in range(sh.P):
-                    assert np.array_equal(g["gathered"][rr * sh.T + t], q)
-                    assert np.array_equal(g["gathered_scales"][rr * sh.T + t], sc)
-            e = int(o_ids[t, j])
-            stub_rows[r, j] = orc.stub_row(sh, e, q, sc)
-            assert np.array_equal(g["expert_out"][qq], stub_rows[r, j])
-            if not direct:              # the base combine also serves the all-gather dispatch
-                assert np.array_equal(g["comb"][t * sh.k + j], stub_rows[r, j])
-    red = orc.reduce_tokens(sh, tokens, stub_rows, o_w)
-    assert_y_close(g["y"][tokens], red["y32"])
-    if np.array_equal(g["w"][tokens], o_w[tokens]):
-        assert np.array_equal(g["y"][tokens], red["y"])
-    del nb
+    for key in ("send_rows", "recv_rows", "send_scales", "recv_scales", "expert_out", "comb"):
+        if g[key] is None:             # the direct and all-gather forms keep no send side; direct no comb
+            assert (key.startswith("send") and (direct or allgather)) or (key == "comb" and direct), key
+            continue
+        assert np.array_equal(g[key].view(np.uint8), o[key].view(np.uint8)), key
+        g[key] = None                   # keep the host copies of a 4 GB problem bounded
+    assert record_weights_match(g["recv_meta"], g["w"], g["recv_pos"])
+    assert_y_close(g["y"], o["y32"], o["y"])
+    if weights_equal(g["w"], o["w"]):
+        assert_bf16_equal(g["y"], o["y"])
+    if allgather:
+        # token t's dispatched codes and scales are the oracle's receive row of its slot 0
+        q0 = o["recv_pos"][:, 0]
+        codes, scales = o["recv_rows"][q0], o["recv_scales"][q0]
+        for r in range(sh.P):
+            assert np.array_equal(g["gathered"][r * sh.T:(r + 1) * sh.T], codes), ("gathered rows", r)
+            assert np.array_equal(g["gathered_scales"][r * sh.T:(r + 1) * sh.T].view(np.uint32),
+                                  scales.view(np.uint32)), ("gathered scales", r)
 
 
 def test_worked_example_on_gpu(orc):
@@ -260,6 +243,62 @@ def test_extreme_skew_and_ties_in_logits(orc, E, k):
     _full_parity(orc, sh, wl.make_hidden(4, sh.T, H), logits=logits, label=f"skew+ties E={E}")
 
 
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 8), (96, 8), (256, 8)])
+def test_route_nan_logits(orc, E, k):
+    """NaN logits rank below every number and tie with each other (lower id first), in
+    both router shapes; the rows that hold one get NaN weights on both sides, and the
+    whole path then carries those NaNs to the same y positions as the oracle."""
+    P, Tp, H = 4, 32, 128
+    sh = orc.Shape(P, P * Tp, E, k, H, False)
+    rng = np.random.default_rng(23)
+    logits = rng.integers(-3, 4, size=(sh.T, E)).astype(np.float32)
+    logits[rng.random((sh.T, E)) < 0.05] = np.nan
+    logits[0] = np.nan                        # a whole row of NaN
+    logits[1, 0] = np.nan                     # NaN before every number
+    logits[2] = -np.inf
+    logits[2, E - 1] = np.nan                 # NaN after a row of -inf
+    logits[3, : E - k + 1] = np.nan           # fewer numbers than slots
+    logits[4] = rng.normal(size=E)            # no NaN at all
+    logits[5, 3] = np.frombuffer(np.uint32(0xFFC00000).tobytes(), np.float32)[0]   # a negative NaN
+    _full_parity(orc, sh, wl.make_hidden(11, sh.T, H), logits=logits, label=f"NaN logits E={E}")
+
+
+def test_fp8_hardware_conversions(orc):
+    """The FP8 encoder (v_cvt_pk_fp8_f32) and decoder (v_cvt_pk_f32_fp8) against the oracle's
+    E4M3 conversions written from the format's definition.  Every bf16 value of magnitude <= 448
+    sits in a block whose maximum is 448, so the scale is exactly 1 and the code is the plain
+    nearest-even E4M3 of the value; those codes cover all 254 finite codes, and the expert stub
+    of expert 0 (multiplier exactly 1) writes each code's decoded value back, so expert_out
+    checks the decoder.  Two more rows of normal values quantise under arbitrary scales."""
+    H = 7168
+    per_block = 127
+    mags = np.arange(0x0000, 0x43E1, dtype=np.uint16)                 # bf16 0 .. 448
+    vals = np.concatenate([mags, mags | np.uint16(0x8000)])           # and their negatives
+    nblk = -(-len(vals) // per_block)
+    rows = -(-nblk // (H // 128))
+    P, Tp = 2, (rows + 2 + 1) // 2
+    T = P * Tp
+    x = wl.make_hidden(29, T, H)
+    blocks = np.zeros((rows * (H // 128), 128), np.uint16)
+    padded = np.zeros(nblk * per_block, np.uint16)
+    padded[: len(vals)] = vals
+    blocks[:nblk, :per_block] = padded.reshape(nblk, per_block)
+    blocks[:, per_block] = 0x43E0                                     # 448: amax 448, scale exactly 1
+    x[:rows] = blocks.reshape(rows, H)
+    sh = orc.Shape(P, T, 4, 1, H, True)
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    g, o = _full_parity(orc, sh, x, ids=ids, w=w, label="fp8 hardware conversions")
+    assert np.all(g["recv_scales"][g["recv_pos"][:rows, 0]] == 1.0)
+    codes = g["recv_rows"][g["recv_pos"][:rows, 0]]
+    finite = np.setdiff1d(np.arange(256), [0x7F, 0xFF])
+    assert np.array_equal(np.unique(codes), finite), "not every finite E4M3 code was produced"
+    # each code's decoded value: the stub of expert 0 multiplies by exactly 1
+    dec = bf16_to_f32(g["expert_out"][g["recv_pos"][:rows, 0]])
+    assert np.array_equal(dec.view(np.uint32), orc.e4m3_to_f32(codes).view(np.uint32))
+    assert np.array_equal(codes, orc.e4m3_from_double(bf16_to_f32(x[:rows]).astype(np.float64)))
+
+
 def test_fp8_special_blocks(orc):
     # zero blocks (scale 0, signed zeros), blocks whose amax is 448 (scale exactly
     # 1, so every e4m3 tie is decided by the rounding rule), tiny and huge values
@@ -290,14 +329,27 @@ def test_fp8_special_blocks(orc):
     _full_parity(orc, sh, x, logits=logits, label="fp8 special blocks")
 
 
-def test_deterministic_and_sentinel_free(orc):
-    w = wl.WORKLOADS["c1"]
+@pytest.mark.parametrize("name,mode", [("c1", "base"), ("c2", "base"), ("c2", "direct"), ("c3", "base"),
+                                       ("c4", "base"), ("c5", "base"), ("c5", "direct")])
+def test_deterministic_and_sentinel_free(orc, name, mode):
+    """Two runs of the same workload, one over buffers pre-filled with 0xFF and one over
+    whatever the allocator hands out, run twice in a row, give identical bytes in every
+    output: no result depends on scheduling, on earlier buffer contents or on a previous call."""
+    w = wl.WORKLOADS[name]
     sh = orc.Shape.of(w)
     inp = wl.make_inputs(w)
-    a = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=True)
-    b = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=False, repeat=2)
-    for key in ("ids", "w", "send_rows", "recv_rows", "expert_out", "comb", "y", "send_pos", "recv_pos"):
-        assert np.array_equal(a[key], b[key]), key
+    log(f"[determinism] {name} {mode}")
+    direct = mode == "direct"
+    a = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=True, direct=direct)
+    b = run_gpu(sh, inp["x"], logits=inp["logits"], sentinel=False, repeat=2, direct=direct)
+    keys = ("ids", "w", "send_meta", "recv_meta", "send_rows", "recv_rows", "send_scales", "recv_scales",
+            "expert_out", "comb", "y") + INT_KEYS
+    for key in keys:
+        if a[key] is None:
+            assert b[key] is None, key
+            continue
+        assert np.array_equal(np.ascontiguousarray(a[key]).view(np.uint8),
+                              np.ascontiguousarray(b[key]).view(np.uint8)), key
 
 
 def test_combine_identity_top1_expert0(orc):
