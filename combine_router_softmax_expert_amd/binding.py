@@ -54,6 +54,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                            "(hipcc --offload-arch=gfx950) first")
+    # torch first: the library and torch must share one HIP runtime, and torch ships
+    # its own.  Loaded first, the library would bring in the system's runtime under
+    # the same soname, and torch would then run on a runtime it was not built with
+    # (its calls then find no device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {

@@ -294,25 +294,22 @@ bool count_is_single(const Dims& d) {
 hipError_t launch_count(const Dims& d, const int32_t* ids, const Workspace& ws, hipStream_t st) {
     if (count_is_single(d)) {
         const int W = single_words(d);
-        launch_kernel(count_scan_single_kernel, dim3(1), dim3(kThreads), single_lds_bytes(d.P, d.E, W), st, ids,
+        return launch_kernel(count_scan_single_kernel, dim3(1), dim3(kThreads), single_lds_bytes(d.P, d.E, W), st, ids,
                            d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n, ws.send_off, ws.C, ws.bucket_rank, ws.N,
                            ws.expert_off, ws.recv_off, ws.rank_recv_off);
-        return hipGetLastError();
     }
     int W = words_per_expert(d.E, d.Tp, 48 * 1024);
     while (W > 1 && 32LL * W * d.k > (long long)kMaxPerThread * kThreads) W /= 2;
     const size_t lds = (2 * (size_t)d.E * W + d.E) * 4;
-    launch_kernel(count_kernel, dim3(d.P), dim3(kThreads), lds, st, ids, d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n,
+    return launch_kernel(count_kernel, dim3(d.P), dim3(kThreads), lds, st, ids, d.Tp, d.E, d.Ep, d.k, d.P, W, ws.n,
                        ws.send_off, ws.C, ws.bucket_rank);
-    return hipGetLastError();
 }
 
 hipError_t launch_scan(const Dims& d, const Workspace& ws, hipStream_t st) {
     const bool stage = ((size_t)d.P * d.E + d.E + 1) * 4 <= kLdsBudget;
     const size_t lds = stage ? ((size_t)d.P * d.E + d.E + 1) * 4 : ((size_t)d.E + 1) * 4;
-    launch_kernel(scan_kernel, dim3(1), dim3(kThreads), lds, st, ws.n, d.P, d.E, d.Ep, stage ? 1 : 0, ws.N,
+    return launch_kernel(scan_kernel, dim3(1), dim3(kThreads), lds, st, ws.n, d.P, d.E, d.Ep, stage ? 1 : 0, ws.N,
                        ws.expert_off, ws.recv_off, ws.rank_recv_off);
-    return hipGetLastError();
 }
 
 }  // namespace moe

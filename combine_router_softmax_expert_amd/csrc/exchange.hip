@@ -195,17 +195,15 @@ hipError_t launch_select(const Dims& d, const Workspace& ws, const int32_t* ids,
     const bool nt = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     if (d.P <= 2 * d.k) {
         auto kernel = nt ? select_scatter_kernel<true> : select_scatter_kernel<false>;
-        launch_kernel(kernel, row_grid((long long)d.P * d.T, slices), dim3(B), 0, st,
+        return launch_kernel(kernel, row_grid((long long)d.P * d.T, slices), dim3(B), 0, st,
                       reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv),
                       recv_scales, ids, ws.recv_pos, d.T, d.Ep, d.k, L, d.scales, slices);
-        return hipGetLastError();
     }
     auto kernel = nt ? select_kernel<true> : select_kernel<false>;
-    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+    return launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                   reinterpret_cast<const uint4*>(gathered), gathered_scales, reinterpret_cast<uint4*>(recv), recv_scales,
                   reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, d.P, d.T, d.Tp, L, d.scales,
                   slices);
-    return hipGetLastError();
 }
 
 hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send, const float* send_scales,
@@ -215,20 +213,18 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (affine) {
-        launch_kernel(exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+        return launch_kernel(exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
                       reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), ws.send_pos, ws.recv_pos,
                       send_scales, recv_scales, reinterpret_cast<const uint4*>(ws.send_meta),
                       reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales, d.k, d.T, token_grid(d, slices, true));
-        return hipGetLastError();
     }
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
-    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+    return launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                   reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
                   gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
                   reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales,
                   slices);
-    return hipGetLastError();
 }
 
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out, uint16_t* comb,
@@ -238,17 +234,16 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (affine)
-        launch_kernel(reverse_exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
-                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L, d.k,
-                      d.T, token_grid(d, slices, true));
-    else if (streaming(d, 2LL * d.Na * 16LL * L))
-        launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
-                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L, slices);
-    else
-        launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
-                      reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                      reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
-    return hipGetLastError();
+        return launch_kernel(reverse_exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+                             reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
+                             d.k, d.T, token_grid(d, slices, true));
+    if (streaming(d, 2LL * d.Na * 16LL * L))
+        return launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+                             reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
+                             slices);
+    return launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+                         reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
+                         reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
 }
 
 }  // namespace moe

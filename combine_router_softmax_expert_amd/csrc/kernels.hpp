@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace moe {
 
 // Events the next kernel launch of this thread records at its start and end
@@ -16,10 +18,18 @@ struct LaunchTiming {
 };
 inline thread_local LaunchTiming launch_timing;
 
-template <typename F, typename... Args>
-inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds_bytes, hipStream_t st, Args... args) {
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds_bytes, st, launch_timing.start, launch_timing.stop, 0u,
-                          args...);
+// Launches `kernel` on `st` and returns the launch's own status (not the
+// thread's last-error slot, which an earlier failing runtime call may hold).
+// The arguments are converted to the kernel's parameter types as
+// hipExtLaunchKernelGGL converts them.
+template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds_bytes, hipStream_t st, Args... args) {
+    auto given = std::tuple<Args...>{args...};
+    auto formal = validateArgsCountType(kernel, given);
+    void* argv[sizeof...(Args) > 0 ? sizeof...(Args) : 1];
+    pArgs<0>(formal, argv);
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds_bytes, st,
+                              launch_timing.start, launch_timing.stop, 0);
 }
 
 // The 16-byte handle record that travels with every dispatched row (the ABI's moe_meta).

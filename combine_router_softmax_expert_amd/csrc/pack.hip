@@ -527,12 +527,11 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
-        launch_kernel(kernel, row_grid(blocks, slices), dim3(B), lds, st,
+        return launch_kernel(kernel, row_grid(blocks, slices), dim3(B), lds, st,
                       reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
                       ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
                       ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
                       L, slices);
-        return hipGetLastError();
     }
     const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = pack_kernel<false, false, false, false>;
@@ -543,11 +542,10 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         if (direct) kernel = nt ? pack_kernel<false, true, false, true> : pack_kernel<false, false, false, true>;
         else kernel = nt ? pack_kernel<false, true, false, false> : pack_kernel<false, false, false, false>;
     }
-    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st,
+    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st,
                   reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
                   reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
                   ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L, slices);
-    return hipGetLastError();
 }
 
 hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w, const Workspace& ws,
@@ -567,16 +565,14 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
                     : mi == 8 ? pick(std::integral_constant<int, 8>{}) : pick(std::integral_constant<int, 16>{});
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
-        launch_kernel(kernel, row_grid(blocks, 1), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
+        return launch_kernel(kernel, row_grid(blocks, 1), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
                       static_cast<uint4*>(nullptr), static_cast<float*>(nullptr), meta, ws.send_to_recv,
                       ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C, ws.expert_off, ws.rank_recv_off,
                       ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P, d.row_units, 1);
-        return hipGetLastError();
     }
     const unsigned blocks = (unsigned)((d.Na + 255) / 256);
-    launch_kernel(handle_kernel, dim3(blocks), dim3(256), 0, st, ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
+    return launch_kernel(handle_kernel, dim3(blocks), dim3(256), 0, st, ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
                   meta, ws.send_pos, ws.recv_pos, (int)d.Na, d.Tp, d.E, d.Ep, d.k);
-    return hipGetLastError();
 }
 
 hipError_t launch_allgather(const Dims& d, const uint16_t* x, void* gathered, float* gathered_scales, hipStream_t st) {
@@ -587,9 +583,8 @@ hipError_t launch_allgather(const Dims& d, const uint16_t* x, void* gathered, fl
     const bool nt = streaming(d, 2LL * d.H * d.T + (long long)d.P * d.T * (16LL * L + 4LL * d.scales));
     auto kernel = d.fp8 ? (nt ? allgather_kernel<true, true, false> : allgather_kernel<true, false, false>)
                         : (nt ? allgather_kernel<false, true, false> : allgather_kernel<false, false, false>);
-    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x),
+    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x),
                   reinterpret_cast<uint4*>(gathered), gathered_scales, d.T, d.P, L, slices);
-    return hipGetLastError();
 }
 
 }  // namespace moe

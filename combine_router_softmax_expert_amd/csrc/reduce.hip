@@ -75,9 +75,8 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
         const int slices = (L + B - 1) / B;
         const TokenGrid tg = token_grid(d, slices, false);
         auto kernel = direct ? reduce_kernel<false, false, true, true> : reduce_kernel<false, false, false, true>;
-        launch_kernel(kernel, tg.grid(), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
+        return launch_kernel(kernel, tg.grid(), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
                       reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, tg);
-        return hipGetLastError();
     }
     const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
     // streaming: two-wave workgroups, seven per 7168-channel row (measured on gfx950 at 8192 tokens x top-8,
@@ -87,9 +86,8 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
     const int slices = (L + B - 1) / B;
     auto kernel = direct ? (nt ? reduce_kernel<true, true, true, false> : reduce_kernel<false, false, true, false>)
                          : (nt ? reduce_kernel<true, true, false, false> : reduce_kernel<false, false, false, false>);
-    launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
+    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
                   reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, TokenGrid{});
-    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -193,9 +193,8 @@ hipError_t launch_rtw(const Dims& d, const float* logits, int32_t* ids, float* w
     constexpr int kThreads = kWave;
     const int tokens_per_block = kThreads / kWave;
     const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
-    launch_kernel((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
+    return launch_kernel((route_topk_wave_kernel<V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w, d.T, d.E,
                        d.k);
-    return hipGetLastError();
 }
 
 template <int G, int V>
@@ -203,9 +202,8 @@ hipError_t launch_rt(const Dims& d, const float* logits, int32_t* ids, float* w,
     constexpr int kThreads = 256;
     const int tokens_per_block = (kThreads / kWave) * (kWave / G);
     const int blocks = (d.T + tokens_per_block - 1) / tokens_per_block;
-    launch_kernel((route_topk_kernel<G, V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w,
+    return launch_kernel((route_topk_kernel<G, V>), dim3(blocks), dim3(kThreads), 0, st, logits, ids, w,
                        d.T, d.E, d.k);
-    return hipGetLastError();
 }
 
 }  // namespace

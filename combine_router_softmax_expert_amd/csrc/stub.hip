@@ -109,21 +109,19 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (affine) {   // bf16 rows
-        launch_kernel(stub_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
+        return launch_kernel(stub_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
                       reinterpret_cast<const uint4*>(recv), reinterpret_cast<const HandleRecord*>(ws.recv_meta),
                       ws.rank_recv_off, ws.recv_pos, reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, d.k, d.T,
                       token_grid(d, slices, true));
-        return hipGetLastError();
     }
     const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
     // streaming: e4m3 rows load and store nontemporally (stub 224 -> 231 us but the reverse exchange
     // after it 320 -> 307 us at 65536 rows: no dirty lines left behind), bf16 rows store nontemporally
     auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, true> : stub_kernel<true, false, false>)
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
-    launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+    return launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
                   reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
                   d.P, d.E, d.Ep, L, slices);
-    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -33,8 +33,7 @@ __global__ __launch_bounds__(256) void validate_ids_kernel(const int32_t* __rest
 }  // namespace
 
 hipError_t launch_validate_ids(const Dims& d, const int32_t* ids, int32_t* bad_out, hipStream_t st) {
-    launch_kernel(validate_ids_kernel, dim3(1), dim3(256), 0, st, ids, d.T, d.E, d.k, bad_out);
-    return hipGetLastError();
+    return launch_kernel(validate_ids_kernel, dim3(1), dim3(256), 0, st, ids, d.T, d.E, d.k, bad_out);
 }
 
 }  // namespace moe
