@@ -10,7 +10,7 @@ machines without the library.
 
 _BINDING_NAMES = {
     "Context", "MoeHandle", "MoeMeta", "MoeError", "moe_route_topk", "moe_dispatch", "moe_expert_stub",
-    "moe_combine", "moe_dispatch_direct", "moe_combine_direct", "moe_dispatch_allgather", "moe_dispatch_send", "moe_dispatch_recv",
+    "moe_combine", "moe_dispatch_direct", "moe_dispatch_noalloc", "moe_combine_direct", "moe_dispatch_allgather", "moe_dispatch_send", "moe_dispatch_recv",
     "moe_combine_send", "moe_combine_recv", "moe_timing_begin", "moe_timing_end", "run_path", "run_overlapped", "lib",
 }
 

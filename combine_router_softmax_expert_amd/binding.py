@@ -73,6 +73,7 @@ def _load():
         "moe_expert_stub": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_combine": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
         "moe_dispatch_direct": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
+        "moe_dispatch_noalloc": (I32, [P, P, P, P, P, P, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_combine_direct": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_dispatch_allgather": (I32, [P, P, P, P, P, SZ, P, P, P, P, ctypes.POINTER(MoeHandle), P]),
         "moe_dispatch_send": (I32, [P, P, P, P, P, SZ, P, P, ctypes.POINTER(MoeHandle), P]),
@@ -249,6 +250,24 @@ def moe_combine(ctx: Context, handle: MoeHandle, expert_out, topk_w, comb_buf, y
                            _ptr(comb_buf, (torch.bfloat16, torch.int16), 2 * Na * H, "comb_buf"),
                            _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
            "moe_combine")
+
+
+def moe_dispatch_noalloc(ctx: Context, x, topk_ids, topk_w, send_buf, send_scales, recv_buf, recv_scales,
+                         stream=None) -> MoeHandle:
+    """moe_dispatch with the library's static workspace in place of a caller buffer."""
+    import torch
+    T, H, k, Na = ctx.T, ctx.H, ctx.k, ctx.num_assignments
+    rb, nb = ctx.row_bytes, ctx.scales_per_row
+    h = MoeHandle()
+    _check(lib.moe_dispatch_noalloc(ctx.handle_ptr, _ptr(x, (torch.bfloat16, torch.int16), 2 * T * H, "x"),
+                                    _ptr(topk_ids, torch.int32, 4 * T * k, "topk_ids"),
+                                    _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
+                                    _ptr(send_buf, None, Na * rb, "send_buf"),
+                                    _ptr(send_scales, torch.float32, 4 * Na * nb, "send_scales"),
+                                    _ptr(recv_buf, None, Na * rb, "recv_buf"),
+                                    _ptr(recv_scales, torch.float32, 4 * Na * nb, "recv_scales"),
+                                    ctypes.byref(h), _stream(stream)), "moe_dispatch_noalloc")
+    return h
 
 
 def moe_dispatch_direct(ctx: Context, x, topk_ids, topk_w, workspace, recv_buf, recv_scales,

@@ -76,6 +76,8 @@ struct moe_ctx {
     uint64_t combine_sent = 0;   // generation whose reverse exchange was issued
     uint64_t direct_sent = 0;    // generation dispatched by moe_dispatch_direct
     void* workspace = nullptr;   // workspace of the latest dispatch (the split receive phase reads its maps)
+    int static_device = -1;      // moe_dispatch_noalloc: the device whose static workspace the latest dispatch used
+    uint64_t static_claim = 0;   // and that dispatch's claim on it (0: the latest dispatch used a caller workspace)
     bool timing = false;
     bool debug = false;    // MOE_EP_DEBUG: validate ids on the device (and synchronise) before dispatching
     std::vector<TimingRecord> records;
@@ -103,10 +105,11 @@ hipEvent_t take_event(moe_ctx* ctx) {
 // Launches one kernel through `fn`; when timing is on, the launch carries a
 // start and a stop event that bracket the kernel's execution.
 template <typename Fn>
-moe_status launch(moe_ctx* ctx, const char* name, hipStream_t st, Fn&& fn) {
+moe_status launch(moe_ctx* ctx, const char* name, hipStream_t st, Fn&& fn, bool timed = true) {
     (void)st;
     hipEvent_t a = nullptr, b = nullptr;
-    if (ctx->timing) {
+    timed = timed && ctx->timing;
+    if (timed) {
         a = take_event(ctx);
         b = take_event(ctx);
         if (!a || !b) return hip_fail(hipErrorOutOfMemory, "hipEventCreate");
@@ -115,7 +118,7 @@ moe_status launch(moe_ctx* ctx, const char* name, hipStream_t st, Fn&& fn) {
     hipError_t e = fn();
     moe::launch_timing = {};
     if (e != hipSuccess) return hip_fail(e, name);
-    if (ctx->timing) ctx->records.push_back({name, a, b});
+    if (timed) ctx->records.push_back({name, a, b});
     return MOE_OK;
 }
 
@@ -162,6 +165,7 @@ bool affine_layout(const moe_ctx* ctx, const moe_handle* h) {
 // receive rows).
 void fill_handle(moe_ctx* ctx, const moe::Workspace& ws, moe_handle* handle, bool with_send) {
     ctx->generation += 1;
+    ctx->static_claim = 0;   // moe_dispatch_noalloc sets its claim after this
     handle->expert_counts = ws.N;
     handle->expert_offsets = ws.expert_off;
     handle->rank_recv_offsets = ws.rank_recv_off;
@@ -197,10 +201,10 @@ moe_status validate_ids(moe_ctx* ctx, const moe::Dims& d, const int32_t* topk_id
 
 // The count kernel (and the scan kernel unless one workgroup does both).
 moe_status count_and_scan(moe_ctx* ctx, const moe::Dims& d, const int32_t* topk_ids, const moe::Workspace& ws,
-                          hipStream_t st) {
-    moe_status s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); });
+                          hipStream_t st, bool timed = true) {
+    moe_status s = launch(ctx, "count", st, [&] { return moe::launch_count(d, topk_ids, ws, st); }, timed);
     if (s == MOE_OK && !moe::count_is_single(d))
-        s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); });
+        s = launch(ctx, "scan", st, [&] { return moe::launch_scan(d, ws, st); }, timed);
     return s;
 }
 
@@ -208,6 +212,9 @@ moe_status check_handle(const moe_ctx* ctx, const moe_handle* h) {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
     if (h->ctx != ctx || h->generation != ctx->generation || ctx->generation == 0)
         return fail(MOE_ERR_STALE_HANDLE, "the handle is not from this ctx's latest dispatch");
+    if (ctx->static_claim != 0 && moe::static_workspace_latest_claim(ctx->static_device) != ctx->static_claim)
+        return fail(MOE_ERR_STALE_HANDLE,
+                    "a later moe_dispatch_noalloc on this device has reused the static workspace the handle points into");
     return MOE_OK;
 }
 
@@ -350,6 +357,54 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t* topk_ids, 
     return launch(ctx, "route_topk", st, [&] { return moe::launch_route_topk(d, logits, topk_ids, topk_w, st); });
 }
 
+}  // extern "C"
+
+namespace {
+
+// The send half of the base dispatch into `workspace` (already checked): count,
+// scan and pack.  `extras` enables per-kernel timing events and the debug-mode
+// id check, which create events or read back to the host.
+moe_status dispatch_send_impl(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                              void* workspace, void* send_buf, float* send_scales, moe_handle* handle,
+                              hipStream_t st, bool extras) {
+    const moe::Dims d = ctx->d;
+    const moe::Workspace ws = carve(ctx, workspace);
+    if (d.T > 0) {
+        moe_status s = extras ? validate_ids(ctx, d, topk_ids, ws, st) : MOE_OK;
+        if (s != MOE_OK) return s;
+        const bool fused = moe::pack_counts(d);
+        if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st, extras);
+        if (s == MOE_OK)
+            s = launch(ctx, fused ? "count_pack" : "pack", st, [&] {
+                return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, false, st);
+            }, extras);
+        if (s != MOE_OK) return s;
+    }
+    ctx->workspace = workspace;
+    fill_handle(ctx, ws, handle, true);
+    return MOE_OK;
+}
+
+// The receive half (the exchange) of the latest base dispatch (handle already checked).
+moe_status dispatch_recv_impl(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
+                              void* recv_buf, float* recv_scales, hipStream_t st, bool extras) {
+    const moe::Dims d = ctx->d;
+    if (d.T > 0) {
+        const moe::Workspace ws = carve(ctx, ctx->workspace);
+        moe_status s = launch(ctx, "exchange", st, [&] {
+            return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, affine_layout(ctx, handle),
+                                        st);
+        }, extras);
+        if (s != MOE_OK) return s;
+    }
+    ctx->received = ctx->generation;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
                              void* workspace, size_t workspace_bytes, void* send_buf, float* send_scales,
                              moe_handle* handle, void* stream) {
@@ -363,23 +418,8 @@ moe_status moe_dispatch_send(moe_ctx* ctx, const uint16_t* x, const int32_t* top
         return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w or send_buf is NULL");
     if (d.fp8 ? (d.T > 0 && !send_scales) : send_scales != nullptr) return bad_scales();
     if (moe_status a = check_alignment({x, send_buf}, {topk_ids, topk_w, send_scales}); a != MOE_OK) return a;
-
-    const moe::Workspace ws = carve(ctx, workspace);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (d.T > 0) {
-        moe_status s = validate_ids(ctx, d, topk_ids, ws, st);
-        if (s != MOE_OK) return s;
-        const bool fused = moe::pack_counts(d);
-        if (!fused) s = count_and_scan(ctx, d, topk_ids, ws, st);
-        if (s == MOE_OK)
-            s = launch(ctx, fused ? "count_pack" : "pack", st, [&] {
-                return moe::launch_pack(d, x, topk_ids, topk_w, ws, send_buf, send_scales, false, st);
-            });
-        if (s != MOE_OK) return s;
-    }
-    ctx->workspace = workspace;
-    fill_handle(ctx, ws, handle, true);
-    return MOE_OK;
+    return dispatch_send_impl(ctx, x, topk_ids, topk_w, workspace, send_buf, send_scales, handle,
+                              static_cast<hipStream_t>(stream), true);
 }
 
 moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void* send_buf, const float* send_scales,
@@ -397,17 +437,8 @@ moe_status moe_dispatch_recv(moe_ctx* ctx, const moe_handle* handle, const void*
     if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales))
         return bad_scales();
     if (moe_status a = check_alignment({send_buf, recv_buf}, {send_scales, recv_scales}); a != MOE_OK) return a;
-    if (d.T > 0) {
-        const moe::Workspace ws = carve(ctx, ctx->workspace);
-        hipStream_t st = static_cast<hipStream_t>(stream);
-        s = launch(ctx, "exchange", st, [&] {
-            return moe::launch_exchange(d, ws, send_buf, send_scales, recv_buf, recv_scales, affine_layout(ctx, handle),
-                                        st);
-        });
-        if (s != MOE_OK) return s;
-    }
-    ctx->received = ctx->generation;
-    return MOE_OK;
+    return dispatch_recv_impl(ctx, handle, send_buf, send_scales, recv_buf, recv_scales,
+                              static_cast<hipStream_t>(stream), true);
 }
 
 moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
@@ -424,6 +455,36 @@ moe_status moe_dispatch(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids
                                      handle, stream);
     if (s != MOE_OK) return s;
     return moe_dispatch_recv(ctx, handle, send_buf, send_scales, recv_buf, recv_scales, stream);
+}
+
+moe_status moe_dispatch_noalloc(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                                void* send_buf, float* send_scales, void* recv_buf, float* recv_scales,
+                                moe_handle* handle, void* stream) {
+    const CallScope scope("moe_dispatch_noalloc");
+    if (!ctx || !handle) return fail(MOE_ERR_INVALID_ARG, "ctx or handle is NULL");
+    const moe::Dims d = ctx->d;
+    if (ctx->ws_bytes > moe::kStaticWorkspaceBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "moe_workspace_bytes(ctx) exceeds the library's static workspace of 8 MiB: use moe_dispatch with "
+                    "a caller workspace");
+    if (d.T > 0 && (!x || !topk_ids || !topk_w || !send_buf || !recv_buf))
+        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w, send_buf or recv_buf is NULL");
+    if (d.fp8 ? (d.T > 0 && (!send_scales || !recv_scales)) : (send_scales || recv_scales)) return bad_scales();
+    if (moe_status a = check_alignment({x, send_buf, recv_buf}, {topk_ids, topk_w, send_scales, recv_scales});
+        a != MOE_OK)
+        return a;
+    int device = -1;
+    void* workspace = nullptr;
+    if (hipError_t e = moe::static_workspace(&device, &workspace); e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // no timing events and no debug read-back here: both would create runtime objects
+    moe_status s = dispatch_send_impl(ctx, x, topk_ids, topk_w, workspace, send_buf, send_scales, handle, st, false);
+    if (s == MOE_OK) s = dispatch_recv_impl(ctx, handle, send_buf, send_scales, recv_buf, recv_scales, st, false);
+    if (s != MOE_OK) return s;
+    ctx->static_device = device;
+    ctx->static_claim = moe::static_workspace_claim(device);
+    return MOE_OK;
 }
 
 moe_status moe_dispatch_direct(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,

@@ -115,6 +115,16 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
 hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
                          bool direct, bool affine, hipStream_t st);
 
+// The library's own dispatch workspace (static_workspace.hip), for moe_dispatch_noalloc.
+constexpr size_t kStaticWorkspaceBytes = 8u << 20;
+// Device address of the current device's copy (taken with hipGetSymbolAddress on
+// first use on that device) and that device's ordinal.
+hipError_t static_workspace(int* device, void** ptr);
+// Marks a dispatch into the device's copy; returns its claim number (1, 2, ...).
+uint64_t static_workspace_claim(int device);
+// The claim number of the latest dispatch into the device's copy.
+uint64_t static_workspace_latest_claim(int device);
+
 inline bool streaming(const Dims& d, long long bytes) {
     return d.policy == CachePolicy::kStreaming || (d.policy == CachePolicy::kAuto && bytes >= kStreamingBytes);
 }

@@ -212,6 +212,31 @@ moe_status moe_expert_stub(moe_ctx* ctx, const moe_handle* handle, const void* r
 moe_status moe_combine(moe_ctx* ctx, const moe_handle* handle, const uint16_t* expert_out,
                        const float* topk_w, uint16_t* comb_buf, uint16_t* y, void* stream);
 
+/* ---- dispatch without a caller workspace ----------------------------------- */
+
+/* moe_dispatch for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels, outputs and handle as moe_dispatch, with the workspace taken
+ * from a static array of 8 MiB that the library holds on each GPU it runs on
+ * (allocated with the code object, kept until the process ends) instead of a
+ * caller buffer.  The call allocates nothing: no hipMalloc or hipFree, no
+ * events (per-kernel timing skips its kernels) and no host read-back (the
+ * MOE_EP_DEBUG id check is not done here).  Nothing in that array has to be
+ * cleared between calls: every dispatch writes each word before reading it.
+ * The handle's arrays point into the current device's copy.  They stay valid
+ * until the next dispatch of this ctx, or the next moe_dispatch_noalloc on the
+ * same device by any ctx; moe_expert_stub and the combines then return
+ * MOE_ERR_STALE_HANDLE.  Every call on one GPU shares that GPU's copy, so
+ * calls that overlap in time on one GPU (other threads, or streams not ordered
+ * after the previous handle's combine) race on it.
+ *   Arguments as moe_dispatch without workspace / workspace_bytes.
+ * Errors: MOE_ERR_WORKSPACE when moe_workspace_bytes(ctx) > 8 MiB (about
+ * 150,000 assignments; the shape then needs moe_dispatch), MOE_ERR_INVALID_ARG,
+ * MOE_ERR_HIP (also when the array's device address cannot be obtained). */
+moe_status moe_dispatch_noalloc(moe_ctx* ctx, const uint16_t* x, const int32_t* topk_ids, const float* topk_w,
+                                void* send_buf, float* send_scales, void* recv_buf, float* recv_scales,
+                                moe_handle* handle, void* stream);
+
 /* ---- direct forms (pack straight into the receive rows, reduce straight from
  * the expert output) ------------------------------------------------------- */
 

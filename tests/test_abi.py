@@ -215,6 +215,36 @@ def test_direct_forms_validate_arguments(b):
     b.lib.moe_ctx_destroy(h0)
 
 
+def test_noalloc_dispatch_validates_arguments(b):
+    """moe_dispatch_noalloc checks its arguments and the size of the static workspace on the
+    host, before it looks up that workspace or enqueues anything."""
+    fake = ctypes.c_void_p(1 << 20)
+    handle = b.MoeHandle()
+    D = b.lib.moe_dispatch_noalloc
+    st, h = _create(b)
+    assert D(None, fake, fake, fake, fake, None, fake, None, ctypes.byref(handle), None) == -1
+    assert D(h, fake, fake, fake, fake, None, fake, None, None, None) == -1
+    assert D(h, fake, fake, fake, None, None, fake, None, ctypes.byref(handle), None) == -1    # no send_buf
+    assert D(h, fake, fake, fake, fake, None, None, None, ctypes.byref(handle), None) == -1    # no recv_buf
+    assert D(h, fake, fake, fake, fake, fake, fake, fake, ctypes.byref(handle), None) == -1    # bf16 takes no scales
+    assert D(h, fake, fake, fake, ctypes.c_void_p((1 << 20) + 8), None, fake, None, ctypes.byref(handle), None) == -1
+    assert b"16-byte" in b.lib.moe_last_error()
+    b.lib.moe_ctx_destroy(h)
+    st, h8 = _create(b, dt=1)
+    assert D(h8, fake, fake, fake, fake, None, fake, fake, ctypes.byref(handle), None) == -1   # e4m3 needs both
+    b.lib.moe_ctx_destroy(h8)
+    # 262144 assignments need more than the 8 MiB the library holds: refused first
+    st, big = _create(b, P=32, Tp=1024, E=256, k=8, H=128)
+    assert st == 0 and b.lib.moe_workspace_bytes(big) > 8 << 20
+    assert D(big, fake, fake, fake, fake, None, fake, None, ctypes.byref(handle), None) == -3
+    assert b"8 MiB" in b.lib.moe_last_error()
+    b.lib.moe_ctx_destroy(big)
+    # the largest workloads here fit: the skewed 32-rank one needs about 3.4 MB
+    st, c5 = _create(b, P=32, Tp=256, E=256, k=8, H=7168, dt=1)
+    assert b.lib.moe_workspace_bytes(c5) < 8 << 20
+    b.lib.moe_ctx_destroy(c5)
+
+
 def test_stale_and_foreign_handles(b):
     st, h = _create(b)
     st2, h2 = _create(b)
