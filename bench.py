@@ -196,6 +196,78 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
                       "copy_tbps": round(2 * nbytes / (ms * 1e-3) / 1e12, 3)}))
 
 
+CEILING_SIZES = (("1GiB", 1 << 30, 10), ("940MB", 939_524_096, 10), ("117MB", 117_440_512, 50),
+                 ("14.7MB", 14_680_064, 500))
+
+
+def ceilings(dev, stream) -> dict:
+    """The library's probe kernels (16-byte units, one per lane, as in the row kernels): a plain copy and a
+    streaming read, temporal and nontemporal, at the sizes of the workloads' row buffers (1 GiB as the
+    HBM reference; 940 MB and 117 MB are the skewed workload's expert output and hidden rows; 14.7 MB the
+    decode workload's row buffers, which stay in the Infinity Cache).  Rates in TB/s of bytes moved
+    (a copy moves 2x its size).  Each figure is the mean of back-to-back launches."""
+    import torch
+
+    from combine_router_softmax_expert_amd import binding as B
+
+    out = {}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    for label, nbytes, reps in CEILING_SIZES:
+        src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for policy, tag in ((B.PROBE_TEMPORAL, "temporal"), (B.PROBE_NONTEMPORAL, "nt"),
+                            (B.PROBE_WRITE_THROUGH, "write_through")):
+            for kind in ("copy", "read"):
+                if kind == "read" and policy == B.PROBE_WRITE_THROUGH:
+                    continue                     # no stores to write through
+                def call():
+                    if kind == "copy":
+                        B.moe_probe_copy(src, dst, policy, stream)
+                    else:
+                        B.moe_probe_read(src, sink, policy == B.PROBE_NONTEMPORAL, stream)
+                call()
+                call()
+                torch.cuda.synchronize()
+                a.record(stream)
+                for _ in range(reps):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / reps
+                moved = (2 if kind == "copy" else 1) * nbytes
+                out[f"{kind}_{tag}_{label}"] = round(moved / (ms * 1e-3) / 1e12, 3)
+        del src, dst
+    # the floor of the decode workload's dispatch+combine as four back-to-back kernels: plain contiguous
+    # copies moving the bytes of its four kernels (pack 16.5 MB, exchange 29.4 MB, reverse exchange
+    # 29.4 MB, reduction 16.5 MB), each reading a buffer written earlier in the chain
+    from combine_router_softmax_expert_amd import workloads as wl
+    kb = kernel_bytes(wl.WORKLOADS["c2"])
+    sizes = [kb[k] // 2 // 16 * 16 for k in ("count_pack", "exchange", "reverse_exchange", "reduce")]
+    bufs = [torch.zeros(max(sizes), dtype=torch.uint8, device=dev) for _ in range(5)]
+
+    for policy, tag in ((B.PROBE_TEMPORAL, "temporal"), (B.PROBE_NONTEMPORAL, "nt"),
+                        (B.PROBE_WRITE_THROUGH, "write_through")):
+        def chain():
+            for i, n in enumerate(sizes):
+                B.moe_probe_copy(bufs[i][:n], bufs[i + 1][:n], policy, stream)
+        for _ in range(20):
+            chain()
+        torch.cuda.synchronize()
+        reps = 500
+        a.record(stream)
+        for _ in range(reps):
+            chain()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        out[f"decode_dc_four_copies_{tag}_us"] = round(us, 3)
+        out[f"decode_dc_four_copies_{tag}_frac_of_8tbps"] = round(2 * sum(sizes) / (us * 1e-6) / 8e12, 4)
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def routing_stats(ids, num_ranks: int, num_experts: int) -> dict:
     """The routing's shape from the expert ids [T, k]: per-expert load imbalance
     (max / mean), empty experts, the share the hottest tenth of the experts takes,
@@ -280,6 +352,227 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
     }
 
 
+class Runner:
+    """One workload's buffers and prepared calls on cuda:0, and the ways it is timed.
+
+    Every timing is a pair of HIP events on the launch stream around back-to-back
+    calls.  ``gated`` first spins the stream for a few tens of milliseconds
+    (torch.cuda._sleep) so that the host enqueues a chunk of calls ahead of the
+    GPU, which then runs them back to back: with per-kernel events each launch
+    costs the host ~15-20 us, more than a decode-sized kernel takes, and without
+    the gate every kernel would start on an idle GPU."""
+
+    CHUNK = 50          # calls enqueued behind one gate
+    GATE_MS = 40.0
+
+    def __init__(self, w, dev, stream, direct=False):
+        import numpy as np
+        import torch
+
+        from combine_router_softmax_expert_amd import binding as B
+        from combine_router_softmax_expert_amd import workloads as wl
+
+        self.B, self.torch, self.np = B, torch, np
+        self.w, self.dev, self.stream, self.direct = w, dev, stream, direct
+        self.inp = wl.make_inputs(w)
+        self.ctx = B.Context.for_workload(w)
+        self.bufs = self.ctx.allocate(dev)
+        self.x = torch.from_numpy(self.inp["x"].view(np.int16)).to(dev)
+        self.logits = torch.from_numpy(self.inp["logits"]).to(dev)
+        # each form's calls with their arguments checked and marshalled once (binding.PreparedPath): the
+        # same library calls and kernels as binding.run_path without its per-call Python work
+        self.paths = {d: B.PreparedPath(self.ctx, self.bufs, self.x, self.logits, stream, direct=d)
+                      for d in (False, True)}
+        self.dcs = {d: B.PreparedPath(self.ctx, self.bufs, self.x, None, stream, direct=d, stages="dispatch_combine")
+                    for d in (False, True)}
+        self.ev0 = torch.cuda.Event(enable_timing=True)
+        self.ev1 = torch.cuda.Event(enable_timing=True)
+        self._cycles_per_ms = None
+
+    def step(self, direct=None):
+        self.paths[self.direct if direct is None else direct]()
+
+    def dispatch_combine(self, direct=None):
+        """Dispatch and combine alone (routing ids/weights and expert outputs from earlier steps)."""
+        self.dcs[self.direct if direct is None else direct]()
+
+    def timed(self, fn, n):
+        """Mean ms of n back-to-back calls, bracketed by synchronize + events on the launch stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        self.ev0.record(self.stream)
+        for _ in range(n):
+            fn()
+        self.ev1.record(self.stream)
+        torch.cuda.synchronize()
+        return self.ev0.elapsed_time(self.ev1) / n
+
+    def _gate(self):
+        torch = self.torch
+        if self._cycles_per_ms is None:       # the spin's clock, once
+            torch.cuda.synchronize()
+            self.ev0.record(self.stream)
+            torch.cuda._sleep(10_000_000)
+            self.ev1.record(self.stream)
+            torch.cuda.synchronize()
+            self._cycles_per_ms = 10_000_000 / max(self.ev0.elapsed_time(self.ev1), 1e-3)
+        torch.cuda._sleep(int(self.GATE_MS * self._cycles_per_ms))
+
+    def gated(self, fn, n):
+        """Mean ms per call of n calls, in chunks that the host enqueues behind a GPU spin."""
+        torch = self.torch
+        total, done = 0.0, 0
+        while done < n:
+            m = min(self.CHUNK, n - done)
+            torch.cuda.synchronize()
+            self._gate()
+            self.ev0.record(self.stream)
+            for _ in range(m):
+                fn()
+            self.ev1.record(self.stream)
+            torch.cuda.synchronize()
+            total += self.ev0.elapsed_time(self.ev1)
+            done += m
+        return total / n
+
+    def kernel_times(self, fn, n, ctxs=None):
+        """Per-kernel mean durations (ms) of n gated calls: every launch carries a start and a stop
+        event in its own dispatch (moe_timing_*).  Returns ({kernel: (launches, total_ms)}, ms per call)."""
+        ctxs = ctxs or [self.ctx]
+        for c in ctxs:
+            self.B.moe_timing_begin(c)
+        ms = self.gated(fn, n)
+        kt = {}
+        for c in ctxs:
+            for name, (launches, tot) in self.B.moe_timing_end(c).items():
+                a, b = kt.get(name, (0, 0.0))
+                kt[name] = (a + launches, b + tot)
+        return kt, ms
+
+    def flushed(self, fn, n):
+        """Median ms of n calls, each after a 1 GiB write that evicts the caches (Infinity Cache included)."""
+        torch, np = self.torch, self.np
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        times = []
+        for _ in range(n):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        del flush
+        return float(np.median(times))
+
+
+def per_kernel_table(kt, kb) -> dict:
+    out = {}
+    for name, (launches, tot) in kt.items():
+        avg = tot / launches
+        out[name] = {"launches": launches, "avg_us": round(avg * 1e3, 3), "algorithmic_bytes": kb[name],
+                     "gbps": round(kb[name] / (avg * 1e-3) / 1e9, 1)}
+    return out
+
+
+def roofline_of(kt, kb, config: str) -> dict:
+    """The dispatch/combine kernel with the largest mean duration: its algorithmic bytes per launch
+    over that duration, against the 8 TB/s HBM peak; traffic from committed counter runs."""
+    dc = {n: v for n, v in kt.items() if PHASE_OF[n] in ("dispatch", "combine")}
+    dom = max(dc, key=lambda n: dc[n][1] / dc[n][0])
+    avg_ms = dc[dom][1] / dc[dom][0]
+    achieved = kb[dom] / (avg_ms * 1e-3) / 1e9
+    return {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(config, dom),
+            "avg_us": round(avg_ms * 1e3, 3), "bytes_per_launch": kb[dom]}
+
+
+def dc_block(w, ms, kb, kt) -> dict:
+    dc_bytes = sum(kb[n] for n in kt if PHASE_OF[n] in ("dispatch", "combine"))
+    return {"ms": round(ms, 5), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1), "algorithmic_bytes": dc_bytes,
+            "gbps": round(dc_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(dc_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_form: bool = True) -> dict:
+    """The figures every H=7168 workload reports: whole steps, dispatch+combine (warm and cache-flushed),
+    the direct form, per-kernel durations and the roofline of the dominant dispatch/combine kernel."""
+    w = r.w
+    kb = kernel_bytes(w)
+    ms_step = r.timed(r.step, steps)
+    dc_ms = r.timed(r.dispatch_combine, steps)
+    kt, ms_with_events = r.kernel_times(r.step, steps)
+    dc_flushed = r.flushed(r.dispatch_combine, flush_runs) if flush_runs else None
+    other = not r.direct
+    other_block = None
+    if other_form:
+        for _ in range(5):
+            r.step(other)
+        other_dc_ms = r.timed(lambda: r.dispatch_combine(other), steps)
+        r.B.moe_timing_begin(r.ctx)
+        r.step(other)                    # once, for the names of the kernels the other form runs
+        kt_other = r.B.moe_timing_end(r.ctx)
+        r.step()                         # leave the buffers as the measured form wrote them
+        other_block = dict(dc_block(w, other_dc_ms, kb, kt_other), mode="base" if r.direct else "direct")
+    phases = {}
+    for name, (launches, tot) in kt.items():
+        phases[PHASE_OF[name]] = phases.get(PHASE_OF[name], 0.0) + tot / launches
+    out = {
+        "workload": w.name, "mode": "direct" if r.direct else "base",
+        "ms_per_step": round(ms_step, 5), "tokens_per_s": round(w.tokens / (ms_step * 1e-3), 1),
+        "dispatch_combine": dc_block(w, dc_ms, kb, kt),
+        "dispatch_combine_cache_flushed": None if dc_flushed is None else dc_block(w, dc_flushed, kb, kt),
+        "other_mode_dispatch_combine": other_block,
+        "kernels": per_kernel_table(kt, kb),
+        "phases_ms": {k: round(v, 5) for k, v in phases.items()},
+        "ms_per_step_with_kernel_events": round(ms_with_events, 5),
+        "roofline": roofline_of(kt, kb, config),
+    }
+    return out
+
+
+def micro_batch_figures(r: "Runner", steps: int, parts: int = 2) -> dict:
+    """Micro-batches through the split phases: the expert stage of one on a second stream overlaps the
+    dispatch and combine of the others.  Wall time on two streams and on one, eagerly and with the host
+    enqueued ahead (gated), against the sum of the schedule's kernel durations (the phases end to end)."""
+    B, torch, w = r.B, r.torch, r.w
+    from combine_router_softmax_expert_amd import workloads as wl
+
+    fp8 = w.dispatch_dtype != "bf16"
+    mb = []
+    for c in range(parts):
+        rows = torch.from_numpy(wl.micro_batch_rows(w.num_ranks, w.tokens_per_rank, parts, c)).to(r.dev)
+        cc = B.Context(w.num_ranks, w.tokens_per_rank // parts, w.num_experts, w.top_k, w.hidden, fp8)
+        mb.append((cc, cc.allocate(r.dev), r.x[rows].contiguous(), r.logits[rows].contiguous()))
+    comm, compute = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def schedule(same_stream):
+        cs = comm if same_stream else compute
+
+        def go():
+            comm.wait_stream(r.stream)
+            cs.wait_stream(r.stream)
+            B.run_overlapped(mb, comm, cs)
+            r.stream.wait_stream(comm)
+            r.stream.wait_stream(cs)
+        return go
+
+    two, one = schedule(False), schedule(True)
+    for _ in range(5):
+        two()
+        one()
+    out = {"parts": parts,
+           "eager_ms_two_streams": round(r.timed(two, steps), 5), "eager_ms_one_stream": round(r.timed(one, steps), 5),
+           "gated_ms_two_streams": round(r.gated(two, steps), 5), "gated_ms_one_stream": round(r.gated(one, steps), 5)}
+    kt, _ = r.kernel_times(one, min(steps, 100), ctxs=[m[0] for m in mb])
+    # the phases end to end: every kernel of the schedule, one after another
+    out["sum_of_kernel_ms"] = round(sum(tot / min(steps, 100) for _, tot in kt.values()), 5)
+    out["saved_by_second_stream_ms"] = round(out["gated_ms_one_stream"] - out["gated_ms_two_streams"], 5)
+    out["tokens_per_s_two_streams"] = round(w.tokens / (out["gated_ms_two_streams"] * 1e-3), 1)
+    del mb
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,12 +588,16 @@ def main():
                     help="comparison runs only: the workload with this many logical ranks instead of its own")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed per-step run")
+    ap.add_argument("--no-flush-run", action="store_true", help="skip the cache-flushed runs")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the blocks of the other H=7168 workloads (byte-model and skewed)")
     ap.add_argument("--core-only", action="store_true",
-                    help="only the timed steps, dispatch+combine and the per-kernel pass (for kernel traces: no "
-                         "other forms, micro-batches or graphs whose launches would mix into the statistics)")
+                    help="only the headline workload's timed steps, dispatch+combine and per-kernel pass (for kernel "
+                         "traces: no other forms, workloads, micro-batches or graphs whose launches would mix in)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only run the copy and streaming-read probes and print their rates")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc outputs into profiles/traffic.json for --config")
     ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
@@ -319,60 +616,36 @@ def main():
         copy_calibration()
         return
 
+    if args.ceilings:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"ceilings_tbps": ceilings(torch.device("cuda:0"), torch.cuda.current_stream())}),
+              flush=True)
+        return
+
     import numpy as np
     import torch
 
-    from combine_router_softmax_expert_amd import binding as B
     from combine_router_softmax_expert_amd import workloads as wl
 
     w = wl.WORKLOADS[args.config]
     if args.ranks:
         w = wl.custom(f"{w.name}-as-ep{args.ranks}", args.ranks, w.tokens, w.num_experts, w.top_k, w.hidden,
                       w.dispatch_dtype, w.seed, w.zipf)
-    inp = wl.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    ctx = B.Context.for_workload(w)
-    bufs = ctx.allocate(dev)
-    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
-    logits = torch.from_numpy(inp["logits"]).to(dev)
     stream = torch.cuda.current_stream()
-
-    direct = args.mode == "direct"
-
-    # Each form's calls with their arguments checked and marshalled once (binding.PreparedPath):
-    # the same library calls and kernels as binding.run_path without its per-call Python work,
-    # which at decode size cost more host time per step than the GPU needs for the step.
-    paths = {d: B.PreparedPath(ctx, bufs, x, logits, stream, direct=d) for d in (False, True)}
-    dcs = {d: B.PreparedPath(ctx, bufs, x, None, stream, direct=d, stages="dispatch_combine") for d in (False, True)}
-
-    def step(direct=direct):
-        paths[direct]()
-
-    def dispatch_combine(direct=direct):
-        """Dispatch and combine alone (routing ids/weights and expert outputs from earlier steps)."""
-        dcs[direct]()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def timed(fn, n):
-        """Mean ms of n back-to-back calls, bracketed by synchronize + events on the launch stream."""
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(n):
-            fn()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / n
+    r = Runner(w, dev, stream, direct=args.mode == "direct")
+    B = r.B
+    extras = not args.core_only
+    flush_runs = 0 if args.no_flush_run else 30
 
     for _ in range(args.warmup):
-        step()
+        r.step()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps of the whole path
-    ms_per_step = timed(step, args.steps)
-    # dispatch + combine alone, K times back to back
-    dc_ms = timed(dispatch_combine, args.steps)
+    # timed region: K back-to-back steps of the whole path (the headline value)
+    ms_per_step = r.timed(r.step, args.steps)
 
     def latency_percentiles(fn, n):
         """Median, p95 and p99 of n back-to-back calls, each bracketed by its own events."""
@@ -387,78 +660,41 @@ def main():
         return {"median": round(float(np.median(t)), 5), "p95": round(float(np.percentile(t, 95)), 5),
                 "p99": round(float(np.percentile(t, 99)), 5)}
 
-    latency_ms = {"step": latency_percentiles(step, args.steps),
-                  "dispatch_combine": latency_percentiles(dispatch_combine, args.steps)}
-
-    # the same K steps with every kernel bracketed by HIP events on its stream
-    # (the library records them around each launch), for per-kernel durations;
-    # each event pair adds launch-to-launch overhead, so these read high for
-    # kernels of a few microseconds
-    B.moe_timing_begin(ctx)
-    ms_with_events = timed(step, args.steps)
-    kt = B.moe_timing_end(ctx)
-
-    extras = not args.core_only
-    other_ms = other_dc_ms = ag_dc_ms = None
-    kt_other, kt_ag, graph, micro = {}, {}, None, None
+    core = measure_core(r, args.steps, 0 if args.core_only else flush_runs, args.config, other_form=extras)
+    latency_ms = None
+    ag = graph = micro = cold_ms = None
     if extras:
-        # the other form of dispatch/combine on the same data, for comparison
-        other = not direct
-        for _ in range(args.warmup):
-            step(other)
-        other_ms = timed(lambda: step(other), args.steps)
-        other_dc_ms = timed(lambda: dispatch_combine(other), args.steps)
-        B.moe_timing_begin(ctx)
-        step(other)                      # once, for the names of the kernels it runs
-        kt_other = B.moe_timing_end(ctx)
-        step()   # leave the buffers as the measured form wrote them
-
+        latency_ms = {"step": latency_percentiles(r.step, args.steps),
+                      "dispatch_combine": latency_percentiles(r.dispatch_combine, args.steps)}
         # the all-gather dispatcher (with the base combine) on the same data
-        gathered, gathered_scales = ctx.allocate_gathered(dev)
-
-        allgather_dc = B.PreparedPath(ctx, bufs, x, None, stream, stages="dispatch_combine", gathered=gathered,
-                                      gathered_scales=gathered_scales)
-
+        gathered, gathered_scales = r.ctx.allocate_gathered(dev)
+        allgather_dc = B.PreparedPath(r.ctx, r.bufs, r.x, None, stream, stages="dispatch_combine",
+                                      gathered=gathered, gathered_scales=gathered_scales)
         for _ in range(args.warmup):
             allgather_dc()
-        ag_dc_ms = timed(allgather_dc, args.steps)
-        B.moe_timing_begin(ctx)
-        timed(allgather_dc, args.steps)
-        kt_ag = B.moe_timing_end(ctx)
+        ag_ms = r.timed(allgather_dc, args.steps)
+        kt_ag, _ = r.kernel_times(allgather_dc, min(args.steps, 200))
+        ag = dict(dc_block(w, ag_ms, kernel_bytes(w), kt_ag),
+                  kernels_us={n: round(v[1] / v[0] * 1e3, 3) for n, v in kt_ag.items()})
         del allgather_dc, gathered, gathered_scales
-        step()   # leave the buffers as the measured form wrote them
+        r.step()   # leave the buffers as the measured form wrote them
+        if flush_runs:
+            cold_ms = r.flushed(r.step, flush_runs)
 
-    # per-step times with the caches flushed before each step (a 1 GiB write)
-    cold_ms = None
-    if extras and not args.no_flush_run:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        times = []
-        for _ in range(min(args.steps, 30)):
-            flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        cold_ms = float(np.median(times))
-        del flush
-
-    if extras:
         # the step captured once in a HIP graph and replayed (no per-call host work)
         def graph_ms(direct):
             g = torch.cuda.CUDAGraph()
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                B.run_path(ctx, bufs, x, logits, None, direct=direct)
+                B.run_path(r.ctx, r.bufs, r.x, r.logits, None, direct=direct)
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             with torch.cuda.graph(g):
-                B.run_path(ctx, bufs, x, logits, None, direct=direct)
+                B.run_path(r.ctx, r.bufs, r.x, r.logits, None, direct=direct)
             for _ in range(args.warmup):
                 g.replay()
-            ms = timed(g.replay, args.steps)
+            ms = r.timed(g.replay, args.steps)
             del g
             return ms
 
@@ -466,56 +702,12 @@ def main():
         for mode, d in (("base", False), ("direct", True)):
             ms = graph_ms(d)
             graph[mode] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
-        # two micro-batches through the split phases: the expert stage of one on a
-        # second stream overlaps the other's dispatch and combine (vs one stream)
-        fp8 = w.dispatch_dtype != "bf16"
-        parts = []
-        for c in range(2):
-            rows = torch.from_numpy(wl.micro_batch_rows(w.num_ranks, w.tokens_per_rank, 2, c)).to(dev)
-            cc = B.Context(w.num_ranks, w.tokens_per_rank // 2, w.num_experts, w.top_k, w.hidden, fp8)
-            parts.append((cc, cc.allocate(dev), x[rows].contiguous(), logits[rows].contiguous()))
-
-        def micro_batches_ms(same_stream):
-            """Eager launches: the host issues 12 calls per step, so at decode sizes this
-            measures the host; large problems measure the GPU."""
-            comm = torch.cuda.Stream()
-            compute = comm if same_stream else torch.cuda.Stream()
-
-            def go():
-                comm.wait_stream(stream)
-                compute.wait_stream(stream)
-                B.run_overlapped(parts, comm, compute)
-                stream.wait_stream(comm)
-                stream.wait_stream(compute)
-
-            for _ in range(args.warmup):
-                go()
-            return timed(go, args.steps)
-
-        mb_two, mb_one = micro_batches_ms(False), micro_batches_ms(True)
-        micro = {"parts": 2, "eager": True, "ms_two_streams": round(mb_two, 5), "ms_one_stream": round(mb_one, 5),
-                 "tokens_per_s_two_streams": round(w.tokens / (mb_two * 1e-3), 1)}
-        del parts
-        step()   # leave the buffers as the measured form wrote them
-
-    kb = kernel_bytes(w)
-    per_kernel = {}
-    phases = {}
-    for name, (launches, tot) in kt.items():
-        avg = tot / launches
-        per_kernel[name] = {"launches": launches, "avg_us": round(avg * 1e3, 3),
-                            "algorithmic_bytes": kb[name],
-                            "gbps": round(kb[name] / (avg * 1e-3) / 1e9, 1)}
-        phases[PHASE_OF[name]] = phases.get(PHASE_OF[name], 0.0) + tot / launches
-    dom = max(kt, key=lambda n: kt[n][1])
-    dom_avg_s = kt[dom][1] / kt[dom][0] * 1e-3
-    achieved = kb[dom] / dom_avg_s / 1e9
-    traffic = load_traffic(args.config, dom)
+        micro = micro_batch_figures(r, min(args.steps, 300))
+        r.step()   # leave the buffers as the measured form wrote them
 
     T = w.tokens
-    dc_bytes = sum(kb[n] for n in kt if PHASE_OF[n] in ("dispatch", "combine"))
-    other_dc_bytes = sum(kb[n] for n in kt_other if PHASE_OF[n] in ("dispatch", "combine"))
-    step_bytes = sum(kb[n] for n in kt)
+    kb = kernel_bytes(w)
+    step_bytes = sum(kb[n] for n in core["kernels"])
     out = {
         "metric": METRIC,
         "value": round(T / (ms_per_step * 1e-3), 1),
@@ -532,40 +724,50 @@ def main():
         "config": {"workload": w.name, "ranks": w.num_ranks, "tokens": T, "experts": w.num_experts,
                    "top_k": w.top_k, "hidden": w.hidden, "dispatch": w.dispatch_dtype,
                    "parallelism": f"ep{w.num_ranks} emulated on 1 GPU", "mode": args.mode},
+        "value_is": "whole step (route, dispatch, expert stub, combine); dispatch_combine.tokens_per_s is the "
+                    "dispatch and combine alone",
         "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "dispatch_combine": {
-            "ms": round(dc_ms, 5), "tokens_per_s": round(T / (dc_ms * 1e-3), 1),
-            "algorithmic_bytes": dc_bytes, "gbps": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "logical_payload_bytes": logical_payload_bytes(w),
-            "logical_payload_gbps": round(logical_payload_bytes(w) / (dc_ms * 1e-3) / 1e9, 1),
-        },
-        "other_mode": None if not extras else {
-            "mode": "base" if direct else "direct",
-            "ms_per_step": round(other_ms, 5), "tokens_per_s": round(T / (other_ms * 1e-3), 1),
-            "dispatch_combine_ms": round(other_dc_ms, 5),
-            "dispatch_combine_tokens_per_s": round(T / (other_dc_ms * 1e-3), 1),
-            "dispatch_combine_gbps": round(other_dc_bytes / (other_dc_ms * 1e-3) / 1e9, 1),
-        },
-        "allgather_dispatch": None if not extras else {
-            "dispatch_combine_ms": round(ag_dc_ms, 5), "dispatch_combine_tokens_per_s": round(T / (ag_dc_ms * 1e-3), 1),
-            "algorithmic_bytes": sum(kb[n] for n in kt_ag if PHASE_OF[n] in ("dispatch", "combine")),
-            "kernels_ms": {n: round(v[1] / v[0], 5) for n, v in kt_ag.items()},
-        },
+        "dispatch_combine": dict(core["dispatch_combine"],
+                                 logical_payload_bytes=logical_payload_bytes(w),
+                                 logical_payload_gbps=round(logical_payload_bytes(w) / (core["dispatch_combine"]["ms"]
+                                                                                        * 1e-3) / 1e9, 1)),
+        "dispatch_combine_cache_flushed": core["dispatch_combine_cache_flushed"],
+        "other_mode": core["other_mode_dispatch_combine"],
+        "allgather_dispatch": ag,
         "graph_replay": graph,
         "micro_batches": micro,
-        "phases_ms": {k: round(v, 5) for k, v in phases.items()},
-        "kernels": per_kernel,
+        "phases_ms": core["phases_ms"],
+        "kernels": core["kernels"],
+        "kernel_timing": "per-kernel HIP events in each launch, the host enqueued ahead of a GPU spin (gated)",
         "latency_ms": latency_ms,
-        "ms_per_step_with_kernel_events": round(ms_with_events, 5),
+        "ms_per_step_with_kernel_events": core["ms_per_step_with_kernel_events"],
         "ms_per_step_cache_flushed": None if cold_ms is None else round(cold_ms, 5),
         "metadata_bytes_per_step": metadata_bytes(w),
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
-        "routing": routing_stats(bufs["topk_ids"].cpu().numpy(), w.num_ranks, w.num_experts),
+        "roofline": core["roofline"],
+        "h7168_workloads": None,
+        "ceilings_tbps": None,
+        "routing": routing_stats(r.bufs["topk_ids"].cpu().numpy(), w.num_ranks, w.num_experts),
         "hardware": host_info(),
         "cpu_baseline": None,
     }
+    inp = r.inp
+    del r
+    torch.cuda.empty_cache()
+    if extras and not args.no_other_configs and not args.ranks:
+        # the other H=7168 workloads the target applies to, each in its own buffers
+        blocks = {}
+        for name in ("c2", "c3", "c5"):
+            if name == args.config:
+                continue
+            o = Runner(wl.WORKLOADS[name], dev, stream, direct=args.mode == "direct")
+            for _ in range(10):
+                o.step()
+            blocks[name] = measure_core(o, min(args.steps, 300), min(flush_runs, 10), name)
+            del o
+            torch.cuda.empty_cache()
+        out["h7168_workloads"] = blocks
+    if extras:
+        out["ceilings_tbps"] = ceilings(dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

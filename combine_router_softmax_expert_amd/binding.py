@@ -80,6 +80,8 @@ def _load():
         "moe_dispatch_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P, P]),
         "moe_combine_send": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P]),
         "moe_combine_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
+        "moe_probe_copy": (I32, [P, P, SZ, I32, P]),
+        "moe_probe_read": (I32, [P, SZ, P, I32, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_begin": (I32, [P]),
@@ -359,6 +361,27 @@ def moe_combine_recv(ctx: Context, handle: MoeHandle, comb_buf, topk_w, y, strea
                                 _ptr(topk_w, torch.float32, 4 * T * k, "topk_w"),
                                 _ptr(y, (torch.bfloat16, torch.int16), 2 * T * H, "y"), _stream(stream)),
            "moe_combine_recv")
+
+
+PROBE_TEMPORAL, PROBE_NONTEMPORAL, PROBE_WRITE_THROUGH = 0, 1, 2
+
+
+def moe_probe_copy(src, dst, policy: int, stream=None):
+    """Measurement aid: dst = src (both contiguous GPU tensors of the same byte size); policy
+    PROBE_TEMPORAL, PROBE_NONTEMPORAL or PROBE_WRITE_THROUGH."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    _check(lib.moe_probe_copy(_ptr(src, name="src"), _ptr(dst, name="dst"), n, int(policy), _stream(stream)),
+           "moe_probe_copy")
+
+
+def moe_probe_read(src, sink, nontemporal: bool, stream=None):
+    """Measurement aid: reads every byte of src; sink is a GPU tensor of at least 256 int32."""
+    import torch
+    n = src.numel() * src.element_size()
+    _check(lib.moe_probe_read(_ptr(src, name="src"), n, _ptr(sink, (torch.int32, torch.uint32), 1024, "sink"),
+                              int(nontemporal), _stream(stream)), "moe_probe_read")
 
 
 def moe_timing_begin(ctx: Context):

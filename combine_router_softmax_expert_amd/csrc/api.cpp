@@ -654,6 +654,28 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
     });
 }
 
+moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, int32_t policy, void* stream) {
+    const CallScope scope("moe_probe_copy");
+    if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src or dst is NULL");
+    if (policy < 0 || policy > 2) return fail(MOE_ERR_INVALID_ARG, "policy must be 0, 1 or 2");
+    if (bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "bytes is not a multiple of 16");
+    if ((bytes / 16) / 256 >= (1ULL << 31)) return fail(MOE_ERR_UNSUPPORTED, "bytes beyond one grid dimension");
+    if (moe_status a = check_alignment({src, dst}, {}); a != MOE_OK) return a;
+    hipError_t e = moe::launch_probe_copy(src, dst, (long long)(bytes / 16), policy, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "probe_copy");
+}
+
+moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal, void* stream) {
+    const CallScope scope("moe_probe_read");
+    if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "src or sink is NULL");
+    if (bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "bytes is not a multiple of 16");
+    if ((bytes / 16) / 256 >= (1ULL << 31)) return fail(MOE_ERR_UNSUPPORTED, "bytes beyond one grid dimension");
+    if (moe_status a = check_alignment({src}, {sink}); a != MOE_OK) return a;
+    hipError_t e = moe::launch_probe_read(src, sink, (long long)(bytes / 16), nontemporal != 0,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "probe_read");
+}
+
 moe_status moe_timing_begin(moe_ctx* ctx) {
     g_last_error.clear();
     if (!ctx) return fail(MOE_ERR_INVALID_ARG, "ctx is NULL");

@@ -115,6 +115,12 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
 hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
                          bool direct, bool affine, hipStream_t st);
 
+// Measurement aids (probe.hip): a plain copy and a streaming read of `units`
+// 16-byte units, one unit per lane; the read's sink holds 256 words.
+// Copy policy: 0 temporal, 1 nontemporal, 2 temporal loads with write-through stores.
+hipError_t launch_probe_copy(const void* src, void* dst, long long units, int policy, hipStream_t st);
+hipError_t launch_probe_read(const void* src, uint32_t* sink, long long units, bool nontemporal, hipStream_t st);
+
 // The library's own dispatch workspace (static_workspace.hip), for moe_dispatch_noalloc.
 constexpr size_t kStaticWorkspaceBytes = 8u << 20;
 // Device address of the current device's copy (taken with hipGetSymbolAddress on

@@ -309,6 +309,27 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
 moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
                             uint16_t* y, void* stream);
 
+/* ---- measurement aids (not part of the path) ------------------------------- */
+
+/* Ceilings of this GPU for the row kernels' access pattern ([A2A] 11.2: read a
+ * kernel's bandwidth against what the hardware delivers, measured the same
+ * way): 16-byte loads (and stores) with one unit per lane, consecutive lanes on
+ * consecutive units.
+ *   moe_probe_copy  dst[0, bytes) = src[0, bytes); policy 0: temporal loads and
+ *                   write-back stores, 1: nontemporal loads and stores, 2:
+ *                   temporal loads and write-through (device-scope) stores, as
+ *                   the row kernels store rows that another XCD reads next
+ *   moe_probe_read  reads src[0, bytes) and discards it, temporal or
+ *                   (nontemporal != 0) nontemporal; sink is a device array of
+ *                   256 uint32 that a lane writes only if its fold of a unit
+ *                   equals 0xA5A5A5A5 (never, for a zero-filled source)
+ * src, dst: device pointers on 16 bytes, bytes a multiple of 16 (else
+ * MOE_ERR_INVALID_ARG, as for a policy outside 0..2; MOE_ERR_UNSUPPORTED
+ * beyond 2^31 workgroups of 4 KiB).  Only enqueue on `stream`; MOE_ERR_HIP if
+ * the launch fails. */
+moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, int32_t policy, void* stream);
+moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal, void* stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 
 /* Static, human-readable text of a status code. */

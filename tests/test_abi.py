@@ -245,6 +245,21 @@ def test_noalloc_dispatch_validates_arguments(b):
     b.lib.moe_ctx_destroy(c5)
 
 
+def test_probes_validate_arguments(b):
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert b.lib.moe_probe_copy(None, fake, 16, 0, None) == -1
+    assert b.lib.moe_probe_copy(fake, None, 16, 1, None) == -1
+    assert b.lib.moe_probe_copy(fake, fake, 17, 0, None) == -1
+    assert b.lib.moe_probe_copy(odd, fake, 16, 0, None) == -1
+    assert b"16-byte" in b.lib.moe_last_error()
+    assert b.lib.moe_probe_read(fake, 16, None, 0, None) == -1
+    assert b.lib.moe_probe_read(None, 16, fake, 0, None) == -1
+    assert b.lib.moe_probe_read(fake, 24, fake, 1, None) == -1
+    assert b.lib.moe_probe_copy(fake, fake, 16, 3, None) == -1    # policies 0..2 only
+    assert b.lib.moe_probe_copy(fake, fake, 0, 0, None) == 0     # nothing to move: nothing enqueued
+
+
 def test_stale_and_foreign_handles(b):
     st, h = _create(b)
     st2, h2 = _create(b)
