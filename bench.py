@@ -200,7 +200,7 @@ CEILING_SIZES = (("1GiB", 1 << 30, 10), ("940MB", 939_524_096, 10), ("117MB", 11
                  ("14.7MB", 14_680_064, 500))
 
 
-def ceilings(dev, stream) -> dict:
+def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
     """The library's probe kernels (16-byte units, one per lane, as in the row kernels): a plain copy and a
     streaming read, temporal and nontemporal, at the sizes of the workloads' row buffers (1 GiB as the
     HBM reference; 940 MB and 117 MB are the skewed workload's expert output and hidden rows; 14.7 MB the
@@ -214,6 +214,7 @@ def ceilings(dev, stream) -> dict:
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     for label, nbytes, reps in CEILING_SIZES:
+        reps = max(2, int(reps * reps_scale))
         src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for policy, tag in ((B.PROBE_TEMPORAL, "temporal"), (B.PROBE_NONTEMPORAL, "nt"),
@@ -254,7 +255,7 @@ def ceilings(dev, stream) -> dict:
         for _ in range(20):
             chain()
         torch.cuda.synchronize()
-        reps = 500
+        reps = max(2, int(500 * reps_scale))
         a.record(stream)
         for _ in range(reps):
             chain()
@@ -350,6 +351,187 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
                    f" ({sh.T} tokens), route+dispatch+stub+combine, {reps} passes in {el:.1f} s, "
                    f"single-threaded C oracle pinned to host core {core}"),
     }
+
+
+# ---------------------------------------------------------------------------
+# summaries of rocprofv3 outputs (profiles/*.md)
+# ---------------------------------------------------------------------------
+
+def _short_kernel(name: str) -> str:
+    return name.replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(", 1)[0]
+
+
+def summarize_trace(config: str, trace_dir: str, command: str) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace` run of `bench.py --core-only`: per path kernel, the
+    launches of the gated per-kernel pass (those after the first GPU spin, which the pass uses as its gate)
+    and, for comparison, all launches, which include the passes whose host pace the profiler slows."""
+    import csv
+    from combine_router_softmax_expert_amd import workloads as wl
+
+    w = wl.WORKLOADS[config]
+    kb = kernel_bytes(w)
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    gated, every, names = {}, {}, {}
+    seen_spin = False
+    for r in rows:
+        if "spin_kernel" in r["Kernel_Name"]:
+            seen_spin = True
+            continue
+        k = path_kernel(r["Kernel_Name"])
+        if k is None:
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        names[k] = _short_kernel(r["Kernel_Name"])
+        every.setdefault(k, []).append(d)
+        if seen_spin:
+            gated.setdefault(k, []).append(d)
+    lines = [f"# Kernel durations: {w.name}", "", f"Workload: {w.describe()}.", "",
+             "Commands (from the repository root, on one MI355X):", "", "```", command,
+             f"python3 bench.py --config {config} --summarize-trace <dir>", "```", "",
+             "Per-kernel durations from `run_kernel_trace.csv`. The \"gated\" columns take the launches of the "
+             "benchmark's per-kernel pass, which enqueues its calls behind a GPU spin so that kernels run back to back "
+             "(the launches after the first `spin_kernel`); these are the durations the benchmark's `kernels` table and "
+             "`roofline` report, measured there with HIP events. \"All launches\" adds the passes before the spin, "
+             "where the profiler's per-dispatch work sets the host's pace and kernels start on an idle GPU.", "",
+             "| kernel | path step | gated calls | gated avg us | gated min us | gated max us | all launches avg us | "
+             "algorithmic MB / launch | GB/s at gated avg | of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    order = sorted(gated, key=lambda k: -sum(gated[k]) / len(gated[k]))
+    total = 0.0
+    for k in order:
+        g = gated[k]
+        avg = sum(g) / len(g)
+        total += avg
+        b = kb[k]
+        lines.append(f"| `{names[k]}` | {k} | {len(g)} | {avg:.3f} | {min(g):.3f} | {max(g):.3f} | "
+                     f"{sum(every[k]) / len(every[k]):.3f} | {b / 1e6:.2f} | {b / avg / 1e3:.0f} | "
+                     f"{b / avg / 1e3 / HBM_PEAK_GBPS:.3f} |")
+    dc = [k for k in order if PHASE_OF[k] in ("dispatch", "combine")]
+    dom = max(dc, key=lambda k: sum(gated[k]) / len(gated[k]))
+    avg = sum(gated[dom]) / len(gated[dom])
+    lines += ["", f"Sum of the gated per-kernel averages: {total:.2f} us per step.", "",
+              f"Roofline kernel (the dispatch or combine kernel with the largest mean): {dom}, {kb[dom]:,} algorithmic "
+              f"bytes per launch / {avg:.3f} us = {kb[dom] / avg / 1e3:.1f} GB/s, "
+              f"{kb[dom] / avg / 1e3 / HBM_PEAK_GBPS:.4f} of 8 TB/s.", ""]
+    return "\n".join(lines)
+
+
+def summarize_traffic(config: str) -> str:
+    """Markdown table of profiles/traffic.json for one workload (calibrated FETCH_SIZE + WRITE_SIZE)."""
+    from combine_router_softmax_expert_amd import workloads as wl
+
+    w = wl.WORKLOADS[config]
+    kb = kernel_bytes(w)
+    t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[config]
+    any_rec = next(iter(t.values()))
+    core = f"python3 bench.py --no-cpu-baseline --core-only --config {config} --steps 3 --warmup 1"
+    lines = [f"# HBM traffic per kernel launch: {w.name}", "", f"Workload: {w.describe()}.", "",
+             "Commands (one counter per run, from the repository root, on one MI355X):", "", "```",
+             f"timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o run -- {core}",
+             f"timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o run -- {core}",
+             "timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -o run -- "
+             "python3 bench.py --copy-calibration",
+             "timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -o run -- "
+             "python3 bench.py --copy-calibration",
+             f"python3 bench.py --config {config} --ingest-counters <fetch_dir> <write_dir> <copy_fetch_dir> "
+             "<copy_write_dir>",
+             f"python3 bench.py --config {config} --summarize-traffic", "```", "",
+             "Calibration: a plain copy of 1 GiB (`torch.neg` on int32, 1 GiB read + 1 GiB written) reads FETCH_SIZE "
+             f"x {any_rec['copy_factor_fetch']} and WRITE_SIZE x {any_rec['copy_factor_write']} of its known bytes; "
+             "every kernel's counters are scaled by these factors. FETCH_SIZE / WRITE_SIZE count L2 <-> fabric "
+             "traffic: bytes the Infinity Cache serves count as fetched.", "",
+             "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | traffic MB/launch (calibrated) | "
+             "algorithmic MB/launch | traffic / algorithmic |", "|---|---|---|---|---|---|"]
+    for k, r in sorted(t.items(), key=lambda kv: -(kv[1]["fetch_bytes"] + kv[1]["write_bytes"])):
+        tot = r["fetch_bytes"] + r["write_bytes"]
+        lines.append(f"| {k} | {r['fetch_kib_per_dispatch']} | {r['write_kib_per_dispatch']} | {tot / 1e6:.2f} | "
+                     f"{kb[k] / 1e6:.2f} | {tot / kb[k]:.3f} |")
+    lines += ["", "Source hashes the figures were taken on (bench.py drops `traffic` once a kernel's source changes): "
+              + ", ".join(f"{k} `{r['source_sha']}`" for k, r in sorted(t.items())), ""]
+    return "\n".join(lines)
+
+
+COUNTER_PASSES = (
+    ("l2", "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum"),
+    ("lat", "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_DRAM_sum TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum "
+            "TCP_TCC_WRITE_REQ_sum TCP_TCC_WRITE_REQ_LATENCY_sum"),
+    ("occ", "OccupancyPercent MeanOccupancyPerCU SQ_WAVES GRBM_GUI_ACTIVE"),
+)
+
+
+def _counters_by(d: str, key) -> dict:
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = key(r)
+            if k is None:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def summarize_counters(config: str, path_dirs: list, probe_dirs: list) -> str:
+    """Markdown table of the cache, latency and occupancy counters (COUNTER_PASSES) of the path's kernels,
+    next to the probe copies and reads of the same sizes, per dispatch."""
+    from combine_router_softmax_expert_amd import workloads as wl
+
+    w = wl.WORKLOADS[config]
+
+    def path_key(r):
+        return path_kernel(r["Kernel_Name"])
+
+    def probe_key(r):
+        n = r["Kernel_Name"]
+        if "probe_" not in n:
+            return None
+        pol = n.split("<", 1)[1].split(">", 1)[0]
+        label = {"0": "temporal", "1": "nontemporal", "2": "write-through", "false": "temporal",
+                 "true": "nontemporal"}[pol]
+        mb = int(r["Grid_Size"]) * 16 / 1e6
+        return f"probe {'copy' if 'copy' in n else 'read'} {mb:.1f} MB, {label}"
+
+    def merged(dirs, key):
+        out = {}
+        for d in dirs:
+            for k, cs in _counters_by(d, key).items():
+                out.setdefault(k, {}).update(cs)
+        return out
+
+    rows = list(merged(path_dirs, path_key).items()) + sorted(merged(probe_dirs, probe_key).items())
+    core = f"python3 bench.py --no-cpu-baseline --core-only --config {config} --steps 3 --warmup 1"
+    probe = "python3 bench.py --ceilings --reps-scale 0.02"
+    lines = [f"# Cache, latency and occupancy counters: {w.name} and the probe kernels", "",
+             f"Workload: {w.describe()}.", "", "Commands (one pass per line, each for the path and for the probes; from "
+             "the repository root, on one MI355X):", "", "```"]
+    for name, counters in COUNTER_PASSES:
+        lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {counters} --output-format csv -d <{name}_dir> -o run -- "
+                     f"{core}")
+        lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {counters} --output-format csv -d <{name}_probe_dir> -o "
+                     f"run -- {probe}")
+    lines += [f"python3 bench.py --config {config} --summarize-counters <l2_dir> <lat_dir> <occ_dir> "
+              "<l2_probe_dir> <lat_probe_dir> <occ_probe_dir>", "```", "",
+              "Per dispatch, mean over the dispatches of each kernel (the probes: per size and policy). L2 hit rate = "
+              "TCC_HIT / (TCC_HIT + TCC_MISS). EA reads and writes are the L2's requests to the fabric (64 or 128 "
+              "bytes each); every one is counted as destined for DRAM, because the Infinity Cache sits on the memory "
+              "side of the fabric and gfx950 exposes no counter that splits its hits from HBM accesses. Latencies "
+              "are TCP_TCC_*_REQ_LATENCY / TCP_TCC_*_REQ, in cycles, from the vector cache to the L2 and back. "
+              "Occupancy is rocprofv3's derived OccupancyPercent and MeanOccupancyPerCU (waves resident per CU, of "
+              "32); under counter collection each dispatch's GRBM_GUI_ACTIVE window includes the profiler's own "
+              "overhead, so these read low in absolute terms and compare kernels of similar size.", "",
+              "| kernel | L2 hit % | EA read req | EA write req | read latency (cycles) | write latency (cycles) | "
+              "waves | mean waves / CU | occupancy % |", "|---|---|---|---|---|---|---|---|---|"]
+    for k, c in rows:
+        hit, miss = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        rq, wq = c.get("TCP_TCC_READ_REQ_sum", 0.0), c.get("TCP_TCC_WRITE_REQ_sum", 0.0)
+        rl = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / rq if rq else 0.0
+        wlat = c.get("TCP_TCC_WRITE_REQ_LATENCY_sum", 0.0) / wq if wq else 0.0
+        lines.append(f"| {k} | {100 * hit / max(hit + miss, 1):.1f} | {c.get('TCC_EA0_RDREQ_sum', 0):.0f} | "
+                     f"{c.get('TCC_EA0_WRREQ_sum', 0):.0f} | {rl:.0f} | {wlat:.0f} | {c.get('SQ_WAVES', 0):.0f} | "
+                     f"{c.get('MeanOccupancyPerCU', 0):.2f} | {c.get('OccupancyPercent', 0):.1f} |")
+    lines.append("")
+    return "\n".join(lines)
 
 
 class Runner:
@@ -598,10 +780,29 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only run the copy and streaming-read probes and print their rates")
+    ap.add_argument("--reps-scale", type=float, default=1.0,
+                    help="scale the probes' repetitions (short runs under a counter profiler)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc outputs into profiles/traffic.json for --config")
     ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the markdown summary of a rocprofv3 --kernel-trace run of bench.py --core-only")
+    ap.add_argument("--trace-command", default="", help="command recorded with --summarize-trace")
+    ap.add_argument("--summarize-traffic", action="store_true",
+                    help="print the markdown summary of profiles/traffic.json for --config")
+    ap.add_argument("--summarize-counters", nargs=6, metavar=("L2", "LAT", "OCC", "L2_PROBE", "LAT_PROBE", "OCC_PROBE"),
+                    help="print the markdown summary of the cache, latency and occupancy counter passes")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.config, args.summarize_trace, args.trace_command))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(args.config))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.config, list(args.summarize_counters[:3]), list(args.summarize_counters[3:])))
+        return
 
     if args.ingest_counters:
         ingest_counters(args.config, *args.ingest_counters, copy_bytes=1 << 30, command=args.counter_command)
@@ -619,8 +820,8 @@ def main():
     if args.ceilings:
         import torch
         torch.cuda.set_device(0)
-        print(json.dumps({"ceilings_tbps": ceilings(torch.device("cuda:0"), torch.cuda.current_stream())}),
-              flush=True)
+        print(json.dumps({"ceilings_tbps": ceilings(torch.device("cuda:0"), torch.cuda.current_stream(),
+                                                    args.reps_scale)}), flush=True)
         return
 
     import numpy as np
