@@ -200,18 +200,50 @@ CEILING_SIZES = (("1GiB", 1 << 30, 10), ("940MB", 939_524_096, 10), ("117MB", 11
                  ("14.7MB", 14_680_064, 500))
 
 
+def _spin_cycles_per_ms(stream) -> float:
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(10_000_000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 10_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def gated_ms(fn, n: int, stream, cycles_per_ms: float, chunk: int = 50, gate_ms: float = 40.0) -> float:
+    """Mean ms per call of n calls of fn, enqueued in chunks behind a GPU spin (torch.cuda._sleep), so
+    that the GPU runs each chunk back to back whatever the host's pace; events on `stream`."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total, done = 0.0, 0
+    while done < n:
+        m = min(chunk, n - done)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(gate_ms * cycles_per_ms))
+        a.record(stream)
+        for _ in range(m):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+        done += m
+    return total / n
+
+
 def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
     """The library's probe kernels (16-byte units, one per lane, as in the row kernels): a plain copy and a
-    streaming read, temporal and nontemporal, at the sizes of the workloads' row buffers (1 GiB as the
-    HBM reference; 940 MB and 117 MB are the skewed workload's expert output and hidden rows; 14.7 MB the
-    decode workload's row buffers, which stay in the Infinity Cache).  Rates in TB/s of bytes moved
-    (a copy moves 2x its size).  Each figure is the mean of back-to-back launches."""
+    streaming read, temporal, nontemporal or (copies) with write-through stores, at the sizes of the
+    workloads' row buffers (1 GiB as the HBM reference; 940 MB and 117 MB are the skewed workload's expert
+    output and hidden rows; 14.7 MB the decode workload's row buffers, which stay in the Infinity Cache).
+    Rates in TB/s of bytes moved (a copy moves 2x its size).  Each figure is the mean of launches the GPU
+    runs back to back (enqueued behind a GPU spin, so the host's pace does not enter)."""
     import torch
 
     from combine_router_softmax_expert_amd import binding as B
 
     out = {}
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cpm = _spin_cycles_per_ms(stream)
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     for label, nbytes, reps in CEILING_SIZES:
         reps = max(2, int(reps * reps_scale))
@@ -229,42 +261,29 @@ def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
                         B.moe_probe_read(src, sink, policy == B.PROBE_NONTEMPORAL, stream)
                 call()
                 call()
-                torch.cuda.synchronize()
-                a.record(stream)
-                for _ in range(reps):
-                    call()
-                b.record(stream)
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / reps
+                ms = gated_ms(call, reps, stream, cpm, chunk=min(reps, 100))
                 moved = (2 if kind == "copy" else 1) * nbytes
                 out[f"{kind}_{tag}_{label}"] = round(moved / (ms * 1e-3) / 1e12, 3)
         del src, dst
     # the floor of the decode workload's dispatch+combine as four back-to-back kernels: plain contiguous
     # copies moving the bytes of its four kernels (pack 16.5 MB, exchange 29.4 MB, reverse exchange
-    # 29.4 MB, reduction 16.5 MB), each reading a buffer written earlier in the chain
+    # 29.4 MB, reduction 16.5 MB), each reading the buffer the copy before it wrote
     from combine_router_softmax_expert_amd import workloads as wl
     kb = kernel_bytes(wl.WORKLOADS["c2"])
     sizes = [kb[k] // 2 // 16 * 16 for k in ("count_pack", "exchange", "reverse_exchange", "reduce")]
     bufs = [torch.zeros(max(sizes), dtype=torch.uint8, device=dev) for _ in range(5)]
-
+    views = [(bufs[i][:n], bufs[i + 1][:n]) for i, n in enumerate(sizes)]
     for policy, tag in ((B.PROBE_TEMPORAL, "temporal"), (B.PROBE_NONTEMPORAL, "nt"),
                         (B.PROBE_WRITE_THROUGH, "write_through")):
         def chain():
-            for i, n in enumerate(sizes):
-                B.moe_probe_copy(bufs[i][:n], bufs[i + 1][:n], policy, stream)
-        for _ in range(20):
+            for s_, d_ in views:
+                B.moe_probe_copy(s_, d_, policy, stream)
+        for _ in range(5):
             chain()
-        torch.cuda.synchronize()
-        reps = max(2, int(500 * reps_scale))
-        a.record(stream)
-        for _ in range(reps):
-            chain()
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / reps * 1e3
+        us = gated_ms(chain, max(2, int(500 * reps_scale)), stream, cpm, chunk=25) * 1e3
         out[f"decode_dc_four_copies_{tag}_us"] = round(us, 3)
         out[f"decode_dc_four_copies_{tag}_frac_of_8tbps"] = round(2 * sum(sizes) / (us * 1e-6) / 8e12, 4)
-    del bufs
+    del bufs, views
     torch.cuda.empty_cache()
     return out
 
@@ -589,33 +608,11 @@ class Runner:
         torch.cuda.synchronize()
         return self.ev0.elapsed_time(self.ev1) / n
 
-    def _gate(self):
-        torch = self.torch
-        if self._cycles_per_ms is None:       # the spin's clock, once
-            torch.cuda.synchronize()
-            self.ev0.record(self.stream)
-            torch.cuda._sleep(10_000_000)
-            self.ev1.record(self.stream)
-            torch.cuda.synchronize()
-            self._cycles_per_ms = 10_000_000 / max(self.ev0.elapsed_time(self.ev1), 1e-3)
-        torch.cuda._sleep(int(self.GATE_MS * self._cycles_per_ms))
-
     def gated(self, fn, n):
         """Mean ms per call of n calls, in chunks that the host enqueues behind a GPU spin."""
-        torch = self.torch
-        total, done = 0.0, 0
-        while done < n:
-            m = min(self.CHUNK, n - done)
-            torch.cuda.synchronize()
-            self._gate()
-            self.ev0.record(self.stream)
-            for _ in range(m):
-                fn()
-            self.ev1.record(self.stream)
-            torch.cuda.synchronize()
-            total += self.ev0.elapsed_time(self.ev1)
-            done += m
-        return total / n
+        if self._cycles_per_ms is None:       # the spin's clock, once
+            self._cycles_per_ms = _spin_cycles_per_ms(self.stream)
+        return gated_ms(fn, n, self.stream, self._cycles_per_ms, chunk=self.CHUNK, gate_ms=self.GATE_MS)
 
     def kernel_times(self, fn, n, ctxs=None):
         """Per-kernel mean durations (ms) of n gated calls: every launch carries a start and a stop
@@ -683,6 +680,7 @@ def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_fo
     kb = kernel_bytes(w)
     ms_step = r.timed(r.step, steps)
     dc_ms = r.timed(r.dispatch_combine, steps)
+    dc_gated_ms = r.gated(r.dispatch_combine, steps)
     kt, ms_with_events = r.kernel_times(r.step, steps)
     dc_flushed = r.flushed(r.dispatch_combine, flush_runs) if flush_runs else None
     other = not r.direct
@@ -702,7 +700,7 @@ def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_fo
     out = {
         "workload": w.name, "mode": "direct" if r.direct else "base",
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(w.tokens / (ms_step * 1e-3), 1),
-        "dispatch_combine": dc_block(w, dc_ms, kb, kt),
+        "dispatch_combine": dict(dc_block(w, dc_ms, kb, kt), gated_ms=round(dc_gated_ms, 5)),
         "dispatch_combine_cache_flushed": None if dc_flushed is None else dc_block(w, dc_flushed, kb, kt),
         "other_mode_dispatch_combine": other_block,
         "kernels": per_kernel_table(kt, kb),

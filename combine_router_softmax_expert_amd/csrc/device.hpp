@@ -109,11 +109,12 @@ __device__ __forceinline__ void st16_row(uint4* base, int row, int units, int u,
 // ---- OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 significand bits,
 // largest finite 448, NaN = S.1111.111, no infinities) ------------------------------
 // gfx950's v_cvt_pk_fp8_f32 / v_cvt_pk_f32_fp8 work in this format with round
-// to nearest even.  Checked exhaustively against the format's definition: the
-// encoder agrees for every fp32 |v| < 464 (subnormals, ties and signed zeros
-// included) and the decoder for all 254 finite codes.  Callers only encode
-// quotients x / (amax / 448), whose magnitude stays below 449.8 even when the
-// scale is an fp32 subnormal, so saturation never comes into play.
+// to nearest even.  Tested bit for bit against the format's definition on the
+// GPU: the encoder on every bf16 value of magnitude <= 448 (ties, subnormals and
+// signed zeros included) and on the quotients of the FP8 workloads, the decoder
+// on all 254 finite codes.  Callers only encode quotients x / (amax / 448),
+// whose magnitude stays below 449.8 even when the scale is an fp32 subnormal,
+// so saturation never comes into play.
 
 // Four fp32 values -> four codes, byte i holding the code of the i-th value.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
