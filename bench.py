@@ -237,7 +237,9 @@ def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
     workloads' row buffers (1 GiB as the HBM reference; 940 MB and 117 MB are the skewed workload's expert
     output and hidden rows; 14.7 MB the decode workload's row buffers, which stay in the Infinity Cache).
     Rates in TB/s of bytes moved (a copy moves 2x its size).  Each figure is the mean of launches the GPU
-    runs back to back (enqueued behind a GPU spin, so the host's pace does not enter)."""
+    runs back to back (enqueued behind a GPU spin, so the host's pace does not enter).  Then four dependent
+    copies that move the decode workload's dispatch+combine bytes: contiguous, and as row gathers through a
+    random permutation or the identity (microseconds per four copies)."""
     import torch
 
     from combine_router_softmax_expert_amd import binding as B
@@ -284,6 +286,29 @@ def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
         out[f"decode_dc_four_copies_{tag}_us"] = round(us, 3)
         out[f"decode_dc_four_copies_{tag}_frac_of_8tbps"] = round(2 * sum(sizes) / (us * 1e-6) / 8e12, 4)
     del bufs, views
+    # the same four copies in rows of the decode workload's hidden size (577, 1024, 1024 and 576 rows of
+    # 14 KiB), each reading its rows through a seeded random permutation of what the copy before it wrote,
+    # as the path's kernels do (a row is read on another XCD than the one that wrote it 7 times in 8); and
+    # through the identity, which keeps each row on its writer's XCD
+    import numpy as np
+    row = 2 * wl.WORKLOADS["c2"].hidden
+    rows = [n // row for n in sizes]
+    rbufs = [torch.zeros((max(rows), row), dtype=torch.uint8, device=dev) for _ in range(5)]
+    rng = np.random.default_rng(20)
+    perms = {"permuted": [torch.from_numpy(rng.permutation(max(rows))[:n].astype(np.int32)).to(dev) for n in rows],
+             "identity": [torch.arange(n, dtype=torch.int32, device=dev) for n in rows]}
+    for order, policies in (("permuted", ((B.PROBE_TEMPORAL, "temporal"), (B.PROBE_NONTEMPORAL, "nt"),
+                                          (B.PROBE_WRITE_THROUGH, "write_through"))),
+                            ("identity", ((B.PROBE_WRITE_THROUGH, "write_through"),))):
+        for policy, tag in policies:
+            def chain():
+                for i, n in enumerate(rows):
+                    B.moe_probe_gather(rbufs[i], rbufs[i + 1][:n], perms[order][i], policy, stream)
+            for _ in range(5):
+                chain()
+            us = gated_ms(chain, max(2, int(500 * reps_scale)), stream, cpm, chunk=25) * 1e3
+            out[f"decode_dc_four_row_copies_{order}_{tag}_us"] = round(us, 3)
+    del rbufs, perms
     torch.cuda.empty_cache()
     return out
 

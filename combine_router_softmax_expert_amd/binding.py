@@ -82,6 +82,7 @@ def _load():
         "moe_combine_recv": (I32, [P, ctypes.POINTER(MoeHandle), P, P, P, P]),
         "moe_probe_copy": (I32, [P, P, SZ, I32, P]),
         "moe_probe_read": (I32, [P, SZ, P, I32, P]),
+        "moe_probe_gather": (I32, [P, I32, P, P, I32, I32, I32, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_begin": (I32, [P]),
@@ -382,6 +383,21 @@ def moe_probe_read(src, sink, nontemporal: bool, stream=None):
     n = src.numel() * src.element_size()
     _check(lib.moe_probe_read(_ptr(src, name="src"), n, _ptr(sink, (torch.int32, torch.uint32), 1024, "sink"),
                               int(nontemporal), _stream(stream)), "moe_probe_read")
+
+
+def moe_probe_gather(src, dst, perm, policy: int, stream=None):
+    """Measurement aid: row r of dst = row perm[r] of src.  src [src_rows, row_bytes] and dst [rows,
+    row_bytes] are 2-D uint8 GPU tensors with the same row size; perm holds rows int32 (entries outside
+    [0, src_rows) are clamped into it)."""
+    import torch
+    if src.dim() != 2 or dst.dim() != 2 or src.dtype != torch.uint8 or dst.dtype != torch.uint8:
+        raise ValueError("src and dst must be 2-D uint8 tensors")
+    if src.shape[1] != dst.shape[1]:
+        raise ValueError("src and dst rows differ in size")
+    rows, row_bytes = dst.shape
+    _check(lib.moe_probe_gather(_ptr(src, name="src"), src.shape[0], _ptr(dst, name="dst"),
+                                _ptr(perm, torch.int32, 4 * rows, "perm"), rows, row_bytes, int(policy),
+                                _stream(stream)), "moe_probe_gather")
 
 
 def moe_timing_begin(ctx: Context):

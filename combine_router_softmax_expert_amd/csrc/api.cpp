@@ -665,6 +665,22 @@ moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, int32_t poli
     return e == hipSuccess ? MOE_OK : hip_fail(e, "probe_copy");
 }
 
+moe_status moe_probe_gather(const void* src, int32_t src_rows, void* dst, const int32_t* perm, int32_t rows,
+                            int32_t row_bytes, int32_t policy, void* stream) {
+    const CallScope scope("moe_probe_gather");
+    if (!src || !dst || !perm) return fail(MOE_ERR_INVALID_ARG, "src, dst or perm is NULL");
+    if (policy < 0 || policy > 2) return fail(MOE_ERR_INVALID_ARG, "policy must be 0, 1 or 2");
+    if (rows < 0 || src_rows <= 0) return fail(MOE_ERR_INVALID_ARG, "rows is negative or src_rows is not positive");
+    if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "row_bytes is not a positive multiple of 16");
+    // every row's slices in one grid dimension of fewer than 2^32 work-items (a row takes fewer than 512 more)
+    if ((long long)rows * (row_bytes / 16 + 512) >= (1LL << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "rows x row_bytes beyond one grid dimension");
+    if (moe_status a = check_alignment({src, dst}, {perm}); a != MOE_OK) return a;
+    hipError_t e = moe::launch_probe_gather(src, src_rows, dst, perm, rows, row_bytes / 16, policy,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "probe_gather");
+}
+
 moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal, void* stream) {
     const CallScope scope("moe_probe_read");
     if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "src or sink is NULL");

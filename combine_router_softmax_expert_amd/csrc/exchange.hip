@@ -220,11 +220,13 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     }
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
-    return launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+    const int Bx = gather ? kStreamBlock : B;
+    const int sx = (L + Bx - 1) / Bx;
+    return launch_kernel(kernel, row_grid(d.Na, sx), dim3(Bx), 0, st,
                   reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
                   gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
                   reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales,
-                  slices);
+                  sx);
 }
 
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out, uint16_t* comb,
@@ -237,10 +239,13 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
         return launch_kernel(reverse_exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
                              reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
                              d.k, d.T, token_grid(d, slices, true));
-    if (streaming(d, 2LL * d.Na * 16LL * L))
-        return launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
+    if (streaming(d, 2LL * d.Na * 16LL * L)) {
+        const int Br = kStreamBlock;
+        const int sr = (L + Br - 1) / Br;
+        return launch_kernel(reverse_exchange_gather_kernel, row_grid(d.Na, sr), dim3(Br), 0, st,
                              reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
-                             slices);
+                             sr);
+    }
     return launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                          reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
                          reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);

@@ -120,6 +120,9 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
 // Copy policy: 0 temporal, 1 nontemporal, 2 temporal loads with write-through stores.
 hipError_t launch_probe_copy(const void* src, void* dst, long long units, int policy, hipStream_t st);
 hipError_t launch_probe_read(const void* src, uint32_t* sink, long long units, bool nontemporal, hipStream_t st);
+// Row gather: dst row r (of `units` units) = src row perm[r] clamped into [0, src_rows), r < rows.
+hipError_t launch_probe_gather(const void* src, int src_rows, void* dst, const int32_t* perm, int rows, int units,
+                               int policy, hipStream_t st);
 
 // The library's own dispatch workspace (static_workspace.hip), for moe_dispatch_noalloc.
 constexpr size_t kStaticWorkspaceBytes = 8u << 20;
@@ -141,6 +144,16 @@ inline bool streaming(const Dims& d, long long bytes) {
 // the weighted reduction 5.7 -> 5.9 TB/s against a (rows, slices) grid).  The
 // shape limits keep rows x slices x block below 2^32 work-items.
 inline dim3 row_grid(long long rows, int slices) { return dim3((unsigned)(rows * slices)); }
+
+// Threads per block of the streaming (nontemporal) exchange, reverse exchange
+// and expert stub: one wave, so a row takes L / 64 workgroups.  Measured on
+// gfx950 at 8192 tokens x top-8 x 7168 (65,536 rows) against the row-dividing
+// 448-thread workgroups: exchange of 7 KiB e4m3 rows 159.6 -> 156.1 us, reverse
+// exchange of 14 KiB rows 308.0 -> 302.9 us, e4m3 stub 228.8 -> 220.1 us; at
+// 32,768 rows of 8 KiB each moved by less than 1.5%.  The pack (k stores per
+// lane) ran 8% slower with one wave and the reduction (k loads per lane) no
+// faster, so they keep their sizes.
+constexpr int kStreamBlock = 64;
 
 // Threads per block for a row of `n` per-thread work items: the whole row when it
 // fits in 512 threads, else a divisor of n from 512 down to 256, else 256.

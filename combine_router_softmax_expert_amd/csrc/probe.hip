@@ -8,6 +8,10 @@
 //    1-D grid of 256-thread workgroups, with temporal, nontemporal or
 //    write-through stores: the row kernels' pattern with the permutation taken
 //    out;
+//  - gather: destination row r takes source row perm[r], one unit per lane with
+//    the slices of a row adjacent, as the streaming exchange moves rows: a
+//    chain of such copies, each reading what the one before wrote through a
+//    permutation, has the hand-over of the path's dependent kernels;
 //  - read: the same loads and no stores (each lane folds its unit into a
 //    value that is stored only if it equals a constant no input reaches, so the
 //    loads stay live), the ceiling for kernels that mostly read.
@@ -32,6 +36,21 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const uint4* 
     else st16<POLICY == 1>(&dst[u], v);
 }
 
+// POLICY as probe_copy_kernel.  perm[r] is clamped into [0, src_rows), so no
+// entry can address outside the source.
+template <int POLICY>
+__global__ __launch_bounds__(512) void probe_gather_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ perm, int src_rows, int units,
+                                                           int slices) {
+    const auto [r, slice] = row_slice(slices);
+    const int u = slice * blockDim.x + threadIdx.x;
+    const int p = min(max(perm[r], 0), src_rows - 1);
+    if (u >= units) return;
+    const uint4 v = ld16<POLICY == 1>(&src[(size_t)p * units + u]);
+    if constexpr (POLICY == 0) st16<false>(&dst[(size_t)r * units + u], v);
+    else st16_row<POLICY == 1>(dst, r, units, u, v);   // nontemporal, or write-through
+}
+
 template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ src,
                                                                    uint32_t* __restrict__ sink, long long units,
@@ -51,6 +70,16 @@ hipError_t launch_probe_copy(const void* src, void* dst, long long units, int po
     auto kernel = policy == 1 ? probe_copy_kernel<1> : policy == 2 ? probe_copy_kernel<2> : probe_copy_kernel<0>;
     return launch_kernel(kernel, grid, dim3(kProbeThreads), 0, st, static_cast<const uint4*>(src),
                          static_cast<uint4*>(dst), units);
+}
+
+hipError_t launch_probe_gather(const void* src, int src_rows, void* dst, const int32_t* perm, int rows, int units,
+                              int policy, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const int B = pick_block(units);
+    const int slices = (units + B - 1) / B;
+    auto kernel = policy == 1 ? probe_gather_kernel<1> : policy == 2 ? probe_gather_kernel<2> : probe_gather_kernel<0>;
+    return launch_kernel(kernel, row_grid(rows, slices), dim3(B), 0, st, static_cast<const uint4*>(src),
+                         static_cast<uint4*>(dst), perm, src_rows, units, slices);
 }
 
 hipError_t launch_probe_read(const void* src, uint32_t* sink, long long units, bool nontemporal, hipStream_t st) {

@@ -119,9 +119,11 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     // after it 320 -> 307 us at 65536 rows: no dirty lines left behind), bf16 rows store nontemporally
     auto kernel = d.fp8 ? (nt ? stub_kernel<true, true, true> : stub_kernel<true, false, false>)
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
-    return launch_kernel(kernel, row_grid(d.Na, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
+    const int Bs = nt ? kStreamBlock : B;
+    const int ss = (L + Bs - 1) / Bs;
+    return launch_kernel(kernel, row_grid(d.Na, ss), dim3(Bs), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
                   reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
-                  d.P, d.E, d.Ep, L, slices);
+                  d.P, d.E, d.Ep, L, ss);
 }
 
 }  // namespace moe

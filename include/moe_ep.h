@@ -323,12 +323,25 @@ moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16
  *                   (nontemporal != 0) nontemporal; sink is a device array of
  *                   256 uint32 that a lane writes only if its fold of a unit
  *                   equals 0xA5A5A5A5 (never, for a zero-filled source)
+ *   moe_probe_gather  row r of dst (rows of row_bytes) = row perm[r] of src, for
+ *                   r < rows, with the policies of moe_probe_copy; the
+ *                   streaming exchange's pattern, so that a chain of such
+ *                   copies, each reading through a permutation what the one
+ *                   before wrote, shows the cost of handing rows from one
+ *                   kernel to the next in another order.  perm: device array
+ *                   of `rows` int32; an entry outside [0, src_rows) is clamped
+ *                   into it (src holds src_rows rows).  row_bytes a positive
+ *                   multiple of 16, rows >= 0, src_rows > 0 (else
+ *                   MOE_ERR_INVALID_ARG; MOE_ERR_UNSUPPORTED when
+ *                   rows * (row_bytes / 16 + 512) reaches 2^32).
  * src, dst: device pointers on 16 bytes, bytes a multiple of 16 (else
  * MOE_ERR_INVALID_ARG, as for a policy outside 0..2; MOE_ERR_UNSUPPORTED
  * beyond 2^31 workgroups of 4 KiB).  Only enqueue on `stream`; MOE_ERR_HIP if
  * the launch fails. */
 moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, int32_t policy, void* stream);
 moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal, void* stream);
+moe_status moe_probe_gather(const void* src, int32_t src_rows, void* dst, const int32_t* perm, int32_t rows,
+                            int32_t row_bytes, int32_t policy, void* stream);
 
 /* ---- diagnostics ---------------------------------------------------------- */
 

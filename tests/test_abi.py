@@ -258,6 +258,17 @@ def test_probes_validate_arguments(b):
     assert b.lib.moe_probe_read(fake, 24, fake, 1, None) == -1
     assert b.lib.moe_probe_copy(fake, fake, 16, 3, None) == -1    # policies 0..2 only
     assert b.lib.moe_probe_copy(fake, fake, 0, 0, None) == 0     # nothing to move: nothing enqueued
+    G = b.lib.moe_probe_gather
+    assert G(None, 4, fake, fake, 4, 64, 0, None) == -1             # src, dst and perm must be given
+    assert G(fake, 4, fake, None, 4, 64, 0, None) == -1
+    assert G(fake, 4, fake, fake, 4, 40, 0, None) == -1             # rows of whole 16-byte units
+    assert G(fake, 4, fake, fake, 4, 0, 0, None) == -1
+    assert G(fake, 0, fake, fake, 4, 64, 0, None) == -1             # a source to clamp into
+    assert G(fake, 4, fake, fake, -1, 64, 0, None) == -1
+    assert G(fake, 4, fake, fake, 4, 64, 3, None) == -1             # policies 0..2 only
+    assert G(odd, 4, fake, fake, 4, 64, 0, None) == -1
+    assert G(fake, 4, fake, fake, 1 << 30, 1 << 12, 0, None) == -2  # beyond one grid dimension
+    assert G(fake, 4, fake, fake, 0, 64, 1, None) == 0              # no rows: nothing enqueued
 
 
 def test_stale_and_foreign_handles(b):
