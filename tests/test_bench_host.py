@@ -1,6 +1,6 @@
 """Host logic of bench.py (no GPU): the single-GPU refusal, the algorithmic byte
-model against its closed form, rocprof kernel-name mapping and the counter
-calibration arithmetic."""
+model against its closed form, rocprof kernel-name mapping, the counter
+calibration arithmetic and the kernel-trace summary's choice of launches."""
 
 import csv
 import json
@@ -106,6 +106,41 @@ def test_counter_ingestion_scales_by_the_copy_calibration(tmp_path):
     rec = json.load(open(out))["cX"]["exchange"]
     assert rec["fetch_bytes"] == 2 * 200 * 1024 and rec["write_bytes"] == 400 * 1024
     assert rec["source_sha"] == bench.source_sha("exchange")
+
+
+def test_trace_summary_takes_the_bracketed_pass_only(tmp_path):
+    # launches before the first marker (ungated passes), between the two markers (the per-kernel pass)
+    # and after the second: only the middle ones count as gated
+    rows, t = [], 0
+    def launch(name, us):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": str(t), "End_Timestamp": str(t + int(us * 1000))})
+        t += int(us * 1000) + 500
+    ex = "void moe::(anonymous namespace)::exchange_kernel<false>(x)"
+    launch("at::cuda::(anonymous namespace)::spin_kernel(long)", 50.0)
+    launch(ex, 9.0)
+    launch("void moe::(anonymous namespace)::probe_copy_kernel<0>(x)", 1.0)
+    launch(ex, 5.0)
+    launch(ex, 7.0)
+    launch("void moe::(anonymous namespace)::probe_copy_kernel<0>(x)", 1.0)
+    launch(ex, 20.0)
+    os.makedirs(tmp_path / "tr")
+    with open(tmp_path / "tr" / "run_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows(rows)
+    md = bench.summarize_trace("c2", str(tmp_path / "tr"), "cmd")
+    line = next(x for x in md.splitlines() if x.startswith("| `exchange_kernel"))
+    cells = [c.strip() for c in line.split("|")]
+    assert cells[3] == "2" and cells[4] == "6.000"          # gated calls and mean of the bracketed pair
+    assert cells[7] == "10.250"                            # all four launches
+    os.remove(tmp_path / "tr" / "run_kernel_trace.csv")
+    with open(tmp_path / "tr" / "run_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows([r for r in rows if "probe_copy" not in r["Kernel_Name"]])
+    with pytest.raises(SystemExit):                        # no bracketed pass: refused, not guessed
+        bench.summarize_trace("c2", str(tmp_path / "tr"), "cmd")
 
 
 def test_cpu_baseline_reports_its_sample_cores_and_build(orc):
