@@ -1,8 +1,16 @@
 """Build libmoe_ep.so in-tree: hipcc for gfx950, one object per source, in parallel.
 
 Flags: -O3, IEEE fp32 division (hipcc's default; no fast-math), no implicit
-contraction into fused multiply-adds (the combine's FMAs are explicit), and
-packed fp32 instructions disabled for all device code.
+contraction into fused multiply-adds (the combine's FMAs are explicit),
+packed fp32 instructions disabled for all device code, and kernel arguments
+preloaded into SGPRs: gfx950 can start a wave with the first 16 dwords of its
+kernel arguments (hidden ones such as the workgroup size included, when they
+fit) already in SGPRs, so the wave skips the scalar load of its arguments before
+its first address computation.  The compiler keeps a prologue that loads them
+for firmware that does not preload.  Measured on gfx950, whole step, two
+interleaved runs each: 128 tokens x top-8 x 7168 30.42 -> 29.54 us (dispatch +
+combine 21.10 -> 20.70 us); 2048 tokens x top-2 FP8 68.97 -> 68.10 us; 8192
+tokens x top-8 FP8 966.5 -> 964.6 us.
 """
 
 from __future__ import annotations
@@ -24,6 +32,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC,
 ]
 
