@@ -111,24 +111,21 @@ def load_traffic(config: str, kernel: str):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
-KERNEL_NAME_PATTERNS = (   # rocprofv3 kernel name fragment -> kernel of the path
-    ("route_topk", "route_topk"), ("count_scan_single_kernel", "count"), ("count_kernel", "count"),
-    ("scan_kernel", "scan"), ("count_pack_kernel", "count_pack"), ("pack_kernel", "pack"),
-    ("allgather_kernel", "allgather"), ("handle_kernel", "handles"), ("select_kernel", "select"),
-    ("select_scatter_kernel", "select"), ("reverse_exchange_", "reverse_exchange"),
-    ("exchange_kernel", "exchange"), ("exchange_affine_kernel", "exchange"), ("stub_kernel", "stub"),
-    ("stub_affine_kernel", "stub"), ("reduce_kernel", "reduce"),
+# rocprofv3 kernel name fragment -> kernel of the path, and the position of the template argument that marks
+# the direct form (None: the kernel has no direct form of its own)
+KERNEL_NAME_PATTERNS = (
+    ("route_topk", "route_topk", None), ("count_scan_single_kernel", "count", None), ("count_kernel", "count", None),
+    ("scan_kernel", "scan", None), ("count_pack_kernel", "count_pack", 1), ("pack_kernel", "pack", 3),
+    ("allgather_kernel", "allgather", None), ("handle_kernel", "handles", None), ("select_kernel", "select", None),
+    ("select_scatter_kernel", "select", None), ("reverse_exchange_", "reverse_exchange", None),
+    ("exchange_kernel", "exchange", None), ("exchange_affine_kernel", "exchange", None), ("stub_kernel", "stub", None),
+    ("stub_affine_kernel", "stub", None), ("reduce_kernel", "reduce", 2), ("reduce_affine_kernel", "reduce", 0),
 )
 
 
-# template argument that marks the direct form: position in the argument list
-DIRECT_TEMPLATE_ARG = {"count_pack": 1, "pack": 3, "reduce": 2}
-
-
 def path_kernel(rocprof_name: str):
-    for frag, k in KERNEL_NAME_PATTERNS:
+    for frag, k, i in KERNEL_NAME_PATTERNS:
         if frag in rocprof_name:
-            i = DIRECT_TEMPLATE_ARG.get(k)
             if i is not None:
                 args = [a.strip() for a in rocprof_name.split(frag + "<", 1)[1].split(">", 1)[0].split(",")]
                 if k == "count_pack" and len(args) > 4 and args[4] == "false":

@@ -311,13 +311,15 @@ moe_status moe_ctx_create(const moe_shape* shape, moe_ctx** out) {
     const size_t P = d.P, E = d.E, tk = (size_t)Na;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    ctx->o_n = take(4 * P * E);
-    ctx->o_N = take(4 * E);
-    ctx->o_expert_off = take(4 * (E + 1));
-    ctx->o_rank_recv_off = take(4 * (P + 1));
-    ctx->o_send_off = take(4 * P * E);
-    ctx->o_recv_off = take(4 * E * P);
-    ctx->o_C = take(4 * P * P);
+    const moe::CountLayout cl = moe::count_layout(P, E);   // the count arrays first, as the counting pack expects
+    ctx->o_n = cl.n;
+    ctx->o_N = cl.N;
+    ctx->o_expert_off = cl.expert_off;
+    ctx->o_rank_recv_off = cl.rank_recv_off;
+    ctx->o_send_off = cl.send_off;
+    ctx->o_recv_off = cl.recv_off;
+    ctx->o_C = cl.C;
+    off = cl.end;
     ctx->o_bucket_rank = take(4 * tk);
     ctx->o_send_pos = take(4 * tk);
     ctx->o_recv_pos = take(4 * tk);

@@ -24,16 +24,16 @@ namespace moe {
 namespace {
 
 template <bool GATHER>
-__global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
-                                                       const int32_t* __restrict__ map,
-                                                       const float* __restrict__ send_scales,
-                                                       float* __restrict__ recv_scales,
+__global__ __launch_bounds__(512) void exchange_kernel(const int32_t* __restrict__ map, const uint4* __restrict__ send,
+                                                       uint4* __restrict__ recv, int L, int slices, int bs, int nb,
                                                        const uint4* __restrict__ send_meta,
-                                                       uint4* __restrict__ recv_meta, int L, int nb, int slices) {
+                                                       uint4* __restrict__ recv_meta,
+                                                       const float* __restrict__ send_scales,
+                                                       float* __restrict__ recv_scales) {
     const auto [b, slice] = row_slice(slices);
-    const int u = slice * blockDim.x + threadIdx.x;
+    const int u = slice * bs + threadIdx.x;
     const bool copies_scale = slice == 0 && (int)threadIdx.x < nb;
-    const bool copies_record = slice == 0 && threadIdx.x == blockDim.x - 1;
+    const bool copies_record = slice == 0 && (int)threadIdx.x == bs - 1;
     // The map entry is uniform, so it loads through the scalar cache (the
     // scatter form's row load does not depend on it).  The row's first scales
     // and its record load together with the row, before any store: vmcnt
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512) void exchange_kernel(const uint4* __restrict__
     if (u < L) st16_row<GATHER>(recv, q, L, u, v);
     if (copies_scale) {
         recv_scales[(size_t)q * nb + threadIdx.x] = sc;
-        for (int x = threadIdx.x + blockDim.x; x < nb; x += blockDim.x)   // rows with more scales than threads
+        for (int x = threadIdx.x + bs; x < nb; x += bs)   // rows with more scales than threads
             recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
     }
     if (copies_record) recv_meta[q] = rec;
@@ -86,21 +86,22 @@ __global__ __launch_bounds__(512) void reverse_exchange_gather_kernel(const uint
 // from the handle (every slice of the pack wrote them), then the row.  Their
 // stores are write-back (plain), not st16_row's write-through: the next kernel
 // reads each line on the same XCD, from that L2.
-__global__ __launch_bounds__(512) void exchange_affine_kernel(const uint4* __restrict__ send, uint4* __restrict__ recv,
-                                                              const int32_t* __restrict__ send_pos,
+__global__ __launch_bounds__(512) void exchange_affine_kernel(const int32_t* __restrict__ send_pos,
                                                               const int32_t* __restrict__ recv_pos,
-                                                              const float* __restrict__ send_scales,
-                                                              float* __restrict__ recv_scales,
+                                                              const uint4* __restrict__ send, int L, int k, int T,
+                                                              int bs, int tg_groups, int tg_slices, int tg_tpb_log2,
+                                                              int tg_m_log2, uint4* __restrict__ recv, int nb,
                                                               const uint4* __restrict__ send_meta,
-                                                              uint4* __restrict__ recv_meta, int L, int nb, int k, int T,
-                                                              TokenGrid tg) {
+                                                              uint4* __restrict__ recv_meta,
+                                                              const float* __restrict__ send_scales,
+                                                              float* __restrict__ recv_scales) {
     int t, j, slice;
-    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    if (!token_item(tg_groups, tg_slices, tg_tpb_log2, tg_m_log2, T, t, j, slice)) return;
     const int a = t * k + j;
     const int p = send_pos[a], q = recv_pos[a];
-    const int u = slice * blockDim.x + threadIdx.x;
+    const int u = slice * bs + threadIdx.x;
     const bool copies_scale = slice == 0 && (int)threadIdx.x < nb;
-    const bool copies_record = slice == 0 && threadIdx.x == blockDim.x - 1;
+    const bool copies_record = slice == 0 && (int)threadIdx.x == bs - 1;
     uint4 v, rec;
     float sc;
     if (u < L) v = send[(size_t)p * L + u];
@@ -109,21 +110,22 @@ __global__ __launch_bounds__(512) void exchange_affine_kernel(const uint4* __res
     if (u < L) recv[(size_t)q * L + u] = v;
     if (copies_scale) {
         recv_scales[(size_t)q * nb + threadIdx.x] = sc;
-        for (int x = threadIdx.x + blockDim.x; x < nb; x += blockDim.x)
+        for (int x = threadIdx.x + bs; x < nb; x += bs)
             recv_scales[(size_t)q * nb + x] = send_scales[(size_t)p * nb + x];
     }
     if (copies_record) recv_meta[q] = rec;
 }
 
-__global__ __launch_bounds__(512) void reverse_exchange_affine_kernel(const uint4* __restrict__ expert_out,
-                                                                      uint4* __restrict__ comb,
-                                                                      const int32_t* __restrict__ recv_pos, int L, int k,
-                                                                      int T, TokenGrid tg) {
+__global__ __launch_bounds__(512) void reverse_exchange_affine_kernel(const int32_t* __restrict__ recv_pos,
+                                                                      const uint4* __restrict__ expert_out,
+                                                                      uint4* __restrict__ comb, int L, int k, int T,
+                                                                      int bs, int tg_groups, int tg_slices,
+                                                                      int tg_tpb_log2, int tg_m_log2) {
     int t, j, slice;
-    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    if (!token_item(tg_groups, tg_slices, tg_tpb_log2, tg_m_log2, T, t, j, slice)) return;
     const int a = t * k + j;                    // combine row of the assignment
     const int q = recv_pos[a];
-    const int u = slice * blockDim.x + threadIdx.x;
+    const int u = slice * bs + threadIdx.x;
     if (u < L) comb[(size_t)a * L + u] = expert_out[(size_t)q * L + u];
 }
 
@@ -213,20 +215,20 @@ hipError_t launch_exchange(const Dims& d, const Workspace& ws, const void* send,
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (affine) {
-        return launch_kernel(exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
-                      reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), ws.send_pos, ws.recv_pos,
-                      send_scales, recv_scales, reinterpret_cast<const uint4*>(ws.send_meta),
-                      reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales, d.k, d.T, token_grid(d, slices, true));
+        const TokenGrid tg = token_grid(d, slices, true);
+        return launch_kernel(exchange_affine_kernel, tg.grid(), dim3(B), 0, st, ws.send_pos, ws.recv_pos,
+                             reinterpret_cast<const uint4*>(send), L, d.k, d.T, B, tg.groups, tg.slices, tg.tpb_log2,
+                             tg.m_log2, reinterpret_cast<uint4*>(recv), d.scales, reinterpret_cast<const uint4*>(ws.send_meta),
+                             reinterpret_cast<uint4*>(ws.recv_meta), send_scales, recv_scales);
     }
     const bool gather = streaming(d, 2LL * d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = gather ? exchange_kernel<true> : exchange_kernel<false>;
     const int Bx = gather ? kStreamBlock : B;
     const int sx = (L + Bx - 1) / Bx;
-    return launch_kernel(kernel, row_grid(d.Na, sx), dim3(Bx), 0, st,
-                  reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv),
-                  gather ? ws.recv_to_send : ws.send_to_recv, send_scales, recv_scales,
-                  reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta), L, d.scales,
-                  sx);
+    return launch_kernel(kernel, row_grid(d.Na, sx), dim3(Bx), 0, st, gather ? ws.recv_to_send : ws.send_to_recv,
+                         reinterpret_cast<const uint4*>(send), reinterpret_cast<uint4*>(recv), L, sx, Bx, d.scales,
+                         reinterpret_cast<const uint4*>(ws.send_meta), reinterpret_cast<uint4*>(ws.recv_meta),
+                         send_scales, recv_scales);
 }
 
 hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uint16_t* expert_out, uint16_t* comb,
@@ -235,10 +237,12 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
     const int L = d.out_units;
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
-    if (affine)
-        return launch_kernel(reverse_exchange_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
-                             reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
-                             d.k, d.T, token_grid(d, slices, true));
+    if (affine) {
+        const TokenGrid tg = token_grid(d, slices, true);
+        return launch_kernel(reverse_exchange_affine_kernel, tg.grid(), dim3(B), 0, st, ws.recv_pos,
+                             reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), L, d.k, d.T, B,
+                             tg.groups, tg.slices, tg.tpb_log2, tg.m_log2);
+    }
     if (streaming(d, 2LL * d.Na * 16LL * L)) {
         const int Br = kStreamBlock;
         const int sr = (L + Br - 1) / Br;

@@ -177,20 +177,19 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
 
 template <bool FP8, bool NTL = false, bool NTS = false, bool DIRECT = false>
 __global__ __launch_bounds__(512) void pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
-                                                   const float* __restrict__ w,
                                                    const int32_t* __restrict__ bucket_rank,
                                                    const int32_t* __restrict__ send_off,
-                                                   const int32_t* __restrict__ recv_off,
+                                                   const int32_t* __restrict__ recv_off, int Tp, int E, int k, int L,
+                                                   int slices, int bs, const float* __restrict__ w, int Ep,
                                                    uint4* __restrict__ dst, float* __restrict__ dst_scales,
                                                    HandleRecord* __restrict__ dst_meta, int32_t* __restrict__ send_to_recv,
                                                    int32_t* __restrict__ recv_to_send,
-                                                   int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
-                                                   int Tp, int E, int Ep, int k, int L, int slices) {
+                                                   int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos) {
     __shared__ int32_t pos[32];
     const auto [t, slice] = row_slice(slices);
     const int s = t / Tp;
     const int tid = threadIdx.x;
-    const int u = slice * blockDim.x + tid;   // 16-byte output unit of the row
+    const int u = slice * bs + tid;           // 16-byte output unit of the row
 
     uint4 xa, xb;
     load_row<FP8, NTL>(x, t, L, u, xa, xb);
@@ -289,14 +288,14 @@ __device__ __forceinline__ void wave_prefix_low(const uint64_t* __restrict__ his
 // 16-bit counts (all ids, rank s's ids, the ids of ranks below s), then one
 // wave's prefix sum of the all-ranks and rank-s counts together.
 template <int MI>
-__device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int E, int Ep, int k, int P, int Na,
+__device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int E, int Ep, int k, int P, int Na, int bs,
                             int32_t* __restrict__ n, int32_t* __restrict__ N, int32_t* __restrict__ C,
                             int32_t* __restrict__ expert_off, int32_t* __restrict__ rank_recv_off,
                             int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off) {
     extern __shared__ __align__(16) int32_t lds[];   // E 64-bit entries, then E + 1 prefix sums
     uint64_t* hist = reinterpret_cast<uint64_t*>(lds);
     int32_t* x_s = lds + 2 * E;
-    const int tid = threadIdx.x, bs = blockDim.x;
+    const int tid = threadIdx.x;
     const int lo = s * Tp * k, hi = lo + Tp * k;   // rank s's assignments
     int id[MI];                                  // all loads in flight at once (Na <= MI * bs; clamped
 #pragma unroll                                   // addresses keep the code straight-line, with no wait per load)
@@ -354,28 +353,28 @@ __device__ void rank_counts(const int32_t* __restrict__ ids, int s, int Tp, int 
 // in all: after clearing the histogram, after the atomics, after the positions.
 template <bool FP8, bool DIRECT, int MI, int TPB, bool ROWS = true>
 __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ ids,
-                                                         const float* __restrict__ w, uint4* __restrict__ dst,
-                                                         float* __restrict__ dst_scales,
+                                                         const float* __restrict__ w, int T, int Tp, int E, int k,
+                                                         int L, int slices, int bs, int Ep, int P,
+                                                         uint4* __restrict__ dst, float* __restrict__ dst_scales,
                                                          HandleRecord* __restrict__ dst_meta,
                                                          int32_t* __restrict__ send_to_recv,
                                                          int32_t* __restrict__ recv_to_send,
                                                          int32_t* __restrict__ send_pos, int32_t* __restrict__ recv_pos,
-                                                         int32_t* __restrict__ n, int32_t* __restrict__ N,
-                                                         int32_t* __restrict__ C, int32_t* __restrict__ expert_off,
-                                                         int32_t* __restrict__ rank_recv_off,
-                                                         int32_t* __restrict__ send_off, int32_t* __restrict__ recv_off,
-                                                         int T, int Tp, int E, int Ep, int k, int P, int L,
-                                                         int slices) {
+                                                         int32_t* __restrict__ counts) {
     __shared__ int32_t pos[32];
     __shared__ int32_t blk[32];                // the block's own expert ids
     const auto [b, slice] = row_slice(slices);
-    const int tid = threadIdx.x, bs = blockDim.x;
+    const int tid = threadIdx.x;
     const int Na = T * k;
     const int groups = (T + TPB - 1) / TPB;
     if (b >= groups) {
-        if (slice == 0)
-            rank_counts<MI>(ids, b - groups, Tp, E, Ep, k, P, Na, n, N, C, expert_off, rank_recv_off, send_off,
-                            recv_off);
+        if (slice == 0) {                      // the count arrays from the workspace's start (count_layout)
+            const CountLayout cl = count_layout(P, E);
+            char* base = reinterpret_cast<char*>(counts);
+            auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(base + off); };
+            rank_counts<MI>(ids, b - groups, Tp, E, Ep, k, P, Na, bs, at(cl.n), at(cl.N), at(cl.C), at(cl.expert_off),
+                            at(cl.rank_recv_off), at(cl.send_off), at(cl.recv_off));
+        }
         return;
     }
     const int t0 = b * TPB;
@@ -388,7 +387,7 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
     // the ids first (coalesced, all in flight at once), then the tokens' rows: the
     // counting below waits for the ids only, and LDS-only barriers keep the rows'
     // loads in flight until the rows are stored
-    // (MI ids per thread, MI * blockDim.x >= N_a; straight-line code with clamped
+    // (MI ids per thread, MI * bs >= N_a; straight-line code with clamped
     // addresses, so the waits for the ids do not also wait for the rows)
     int raw[MI];
 #pragma unroll
@@ -527,11 +526,9 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         auto kernel = d.fp8 ? (direct ? pick(T_{}, T_{}) : pick(T_{}, F_{})) : (direct ? pick(F_{}, T_{}) : pick(F_{}, F_{}));
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
-        return launch_kernel(kernel, row_grid(blocks, slices), dim3(B), lds, st,
-                      reinterpret_cast<const uint4*>(x), ids, w, reinterpret_cast<uint4*>(dst), dst_scales, meta,
-                      ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C,
-                      ws.expert_off, ws.rank_recv_off, ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P,
-                      L, slices);
+        return launch_kernel(kernel, row_grid(blocks, slices), dim3(B), lds, st, reinterpret_cast<const uint4*>(x), ids,
+                             w, d.T, d.Tp, d.E, d.k, L, slices, B, d.Ep, d.P, reinterpret_cast<uint4*>(dst), dst_scales,
+                             meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n);
     }
     const bool nt = streaming(d, 2LL * d.H * d.T + d.Na * (16LL * L + 4LL * d.scales));
     auto kernel = pack_kernel<false, false, false, false>;
@@ -542,10 +539,10 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
         if (direct) kernel = nt ? pack_kernel<false, true, false, true> : pack_kernel<false, false, false, true>;
         else kernel = nt ? pack_kernel<false, true, false, false> : pack_kernel<false, false, false, false>;
     }
-    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st,
-                  reinterpret_cast<const uint4*>(x), ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,
-                  reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
-                  ws.recv_pos, d.Tp, d.E, d.Ep, d.k, L, slices);
+    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(x), ids,
+                         ws.bucket_rank, ws.send_off, ws.recv_off, d.Tp, d.E, d.k, L, slices, B, w, d.Ep,
+                         reinterpret_cast<uint4*>(dst), dst_scales, meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
+                         ws.recv_pos);
 }
 
 hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w, const Workspace& ws,
@@ -566,9 +563,9 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
         return launch_kernel(kernel, row_grid(blocks, 1), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
-                      static_cast<uint4*>(nullptr), static_cast<float*>(nullptr), meta, ws.send_to_recv,
-                      ws.recv_to_send, ws.send_pos, ws.recv_pos, ws.n, ws.N, ws.C, ws.expert_off, ws.rank_recv_off,
-                      ws.send_off, ws.recv_off, d.T, d.Tp, d.E, d.Ep, d.k, d.P, d.row_units, 1);
+                             d.T, d.Tp, d.E, d.k, d.row_units, 1, B, d.Ep, d.P, static_cast<uint4*>(nullptr),
+                             static_cast<float*>(nullptr), meta, ws.send_to_recv, ws.recv_to_send, ws.send_pos,
+                             ws.recv_pos, ws.n);
     }
     const unsigned blocks = (unsigned)((d.Na + 255) / 256);
     return launch_kernel(handle_kernel, dim3(blocks), dim3(256), 0, st, ids, w, ws.bucket_rank, ws.send_off, ws.recv_off,

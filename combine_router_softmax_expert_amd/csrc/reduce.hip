@@ -20,22 +20,11 @@ namespace {
 // run in slot order.
 constexpr int kChunk = 8;
 
-// AFFINE: the token-affine grid (token_affine), which serves token t's slice on
-// the XCD whose L2 holds that token's rows; else a row grid over the tokens.
-template <bool NTL, bool NTS, bool DIRECT, bool AFFINE>
-__global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
-                                                     const float* __restrict__ w, uint4* __restrict__ y, int k, int L,
-                                                     int slices, int T, TokenGrid tg) {
-    int t, slice;
-    if constexpr (AFFINE) {
-        int j;
-        if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
-    } else {
-        const RowSlice rs = row_slice(slices);
-        t = rs.row;
-        slice = rs.slice;
-    }
-    const int u = slice * blockDim.x + threadIdx.x;
+// Token t's slice of y, the lane's 16-byte unit u.
+template <bool NTL, bool NTS, bool DIRECT>
+__device__ __forceinline__ void reduce_unit(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
+                                            const float* __restrict__ w, uint4* __restrict__ y, int k, int L, int t,
+                                            int u) {
     if (u >= L) return;
     float acc[8];
 #pragma unroll
@@ -64,6 +53,29 @@ __global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ r
     st16_row<NTS>(y, t, L, u, pack8_bf16(acc));
 }
 
+// Row grid over the tokens (row_grid).
+template <bool NTL, bool NTS, bool DIRECT>
+__global__ __launch_bounds__(512) void reduce_kernel(const uint4* __restrict__ rows, const int32_t* __restrict__ recv_pos,
+                                                     const float* __restrict__ w, uint4* __restrict__ y, int k, int L,
+                                                     int bs, int slices) {
+    const auto [t, slice] = row_slice(slices);
+    reduce_unit<NTL, NTS, DIRECT>(rows, recv_pos, w, y, k, L, t, slice * bs + threadIdx.x);
+}
+
+// The token-affine grid (token_affine), which serves token t's slice on the
+// XCD whose L2 holds that token's rows.  The grid's fields come as scalars: an
+// aggregate argument would end the arguments preloaded into SGPRs.
+template <bool DIRECT>
+__global__ __launch_bounds__(512) void reduce_affine_kernel(const uint4* __restrict__ rows,
+                                                            const int32_t* __restrict__ recv_pos, int k, int L, int bs,
+                                                            int tg_groups, int tg_slices, int tg_tpb_log2,
+                                                            int tg_m_log2, int T, const float* __restrict__ w,
+                                                            uint4* __restrict__ y) {
+    int t, j, slice;
+    if (!token_item(tg_groups, tg_slices, tg_tpb_log2, tg_m_log2, T, t, j, slice)) return;
+    reduce_unit<false, false, DIRECT>(rows, recv_pos, w, y, k, L, t, slice * bs + threadIdx.x);
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* recv_pos, const float* w, uint16_t* y,
@@ -74,9 +86,9 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
         const int B = pick_block(L);
         const int slices = (L + B - 1) / B;
         const TokenGrid tg = token_grid(d, slices, false);
-        auto kernel = direct ? reduce_kernel<false, false, true, true> : reduce_kernel<false, false, false, true>;
-        return launch_kernel(kernel, tg.grid(), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
-                      reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, tg);
+        auto kernel = direct ? reduce_affine_kernel<true> : reduce_affine_kernel<false>;
+        return launch_kernel(kernel, tg.grid(), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, d.k, L,
+                             B, tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, d.T, w, reinterpret_cast<uint4*>(y));
     }
     const bool nt = streaming(d, (d.Na + d.T) * 16LL * L);
     // streaming: two-wave workgroups, seven per 7168-channel row (measured on gfx950 at 8192 tokens x top-8,
@@ -84,10 +96,10 @@ hipError_t launch_reduce(const Dims& d, const uint16_t* rows, const int32_t* rec
     // the temporal sizes below it were as fast or faster with the row-dividing workgroup)
     const int B = nt ? std::min(128, pick_block(L)) : pick_block(L);
     const int slices = (L + B - 1) / B;
-    auto kernel = direct ? (nt ? reduce_kernel<true, true, true, false> : reduce_kernel<false, false, true, false>)
-                         : (nt ? reduce_kernel<true, true, false, false> : reduce_kernel<false, false, false, false>);
-    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos, w,
-                  reinterpret_cast<uint4*>(y), d.k, L, slices, d.T, TokenGrid{});
+    auto kernel = direct ? (nt ? reduce_kernel<true, true, true> : reduce_kernel<false, false, true>)
+                         : (nt ? reduce_kernel<true, true, false> : reduce_kernel<false, false, false>);
+    return launch_kernel(kernel, row_grid(d.T, slices), dim3(B), 0, st, reinterpret_cast<const uint4*>(rows), recv_pos,
+                         w, reinterpret_cast<uint4*>(y), d.k, L, B, slices);
 }
 
 }  // namespace moe

@@ -29,19 +29,19 @@ __device__ __forceinline__ uint4 scale_bf16_unit(const uint4& c, float m) {
 // outputs, so that each wave-wide store covers 1 KiB contiguously (one 16-byte
 // load of adjacent codes with two half-line stores ran 12% slower at 4096 rows
 // and 4% slower at 65536 rows on gfx950; one 8-byte piece per lane, 25% slower).
-// A workgroup slice covers blockDim.x 16-code units, 2 * blockDim.x pieces; a
-// wave covers 128 pieces (blockDim.x is a multiple of 64).
+// A workgroup slice covers bs (the workgroup size) 16-code units, 2 * bs
+// pieces; a wave covers 128 pieces (bs is a multiple of 64).
 template <bool FP8, bool NTL, bool NTS>
-__global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const float* __restrict__ scales,
-                                                   const HandleRecord* __restrict__ meta,
+__global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ recv, const HandleRecord* __restrict__ meta,
                                                    const int32_t* __restrict__ rank_recv_off,
-                                                   uint4* __restrict__ out, int P, int E, int Ep, int L, int slices) {
+                                                   uint4* __restrict__ out, int P, int E, int Ep, int L, int slices,
+                                                   int bs, const float* __restrict__ scales) {
     const auto [q, slice] = row_slice(slices);
     // every load first, unconditional at clamped addresses, so that all of them
     // are in flight before the first wait: one memory round trip in all
     if constexpr (FP8) {
         const int lane = threadIdx.x & (kWave - 1);
-        const int p0 = 2 * (slice * (int)blockDim.x + ((int)threadIdx.x - lane)) + lane;   // 8-code pieces
+        const int p0 = 2 * (slice * bs + ((int)threadIdx.x - lane)) + lane;   // 8-code pieces
         const int p1 = p0 + kWave;
         const int n = 2 * L;                                    // pieces per row
         const uint2* row = reinterpret_cast<const uint2*>(recv) + (size_t)q * n;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
             st16_row<NTS>(out, q, n, p1, pack8_bf16(f));
         }
     } else {
-        const int u = slice * blockDim.x + threadIdx.x;         // 16-byte unit
+        const int u = slice * bs + threadIdx.x;                 // 16-byte unit
         const uint4 c = ld16<NTL>(&recv[(size_t)q * L + min(u, L - 1)]);
         const int local = meta[q].local_expert;
         __builtin_amdgcn_sched_barrier(0);
@@ -83,15 +83,17 @@ __global__ __launch_bounds__(512) void stub_kernel(const uint4* __restrict__ rec
 // Token-affine form for bf16 rows (token_affine): workgroup (t, j, slice) scales
 // receive row recv_pos[t*k + j] on the XCD whose L2 holds what the exchange (or
 // the direct pack) wrote there.
-__global__ __launch_bounds__(512) void stub_affine_kernel(const uint4* __restrict__ recv,
-                                                          const HandleRecord* __restrict__ meta,
+__global__ __launch_bounds__(512) void stub_affine_kernel(const int32_t* __restrict__ recv_pos,
+                                                          const uint4* __restrict__ recv,
+                                                          const HandleRecord* __restrict__ meta, int L, int k, int T,
+                                                          int bs, int tg_groups, int tg_slices, int tg_tpb_log2,
+                                                          int tg_m_log2, uint4* __restrict__ out,
                                                           const int32_t* __restrict__ rank_recv_off,
-                                                          const int32_t* __restrict__ recv_pos, uint4* __restrict__ out,
-                                                          int P, int E, int Ep, int L, int k, int T, TokenGrid tg) {
+                                                          int P, int E, int Ep) {
     int t, j, slice;
-    if (!token_item(tg.groups, tg.slices, tg.tpb_log2, tg.m_log2, T, t, j, slice)) return;
+    if (!token_item(tg_groups, tg_slices, tg_tpb_log2, tg_m_log2, T, t, j, slice)) return;
     const int q = recv_pos[t * k + j];
-    const int u = slice * blockDim.x + threadIdx.x;
+    const int u = slice * bs + threadIdx.x;
     const uint4 c = recv[(size_t)q * L + min(u, L - 1)];
     const int local = meta[q].local_expert;
     __builtin_amdgcn_sched_barrier(0);
@@ -109,10 +111,11 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
     const int B = pick_block(L);
     const int slices = (L + B - 1) / B;
     if (affine) {   // bf16 rows
-        return launch_kernel(stub_affine_kernel, token_grid(d, slices, true).grid(), dim3(B), 0, st,
-                      reinterpret_cast<const uint4*>(recv), reinterpret_cast<const HandleRecord*>(ws.recv_meta),
-                      ws.rank_recv_off, ws.recv_pos, reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, d.k, d.T,
-                      token_grid(d, slices, true));
+        const TokenGrid tg = token_grid(d, slices, true);
+        return launch_kernel(stub_affine_kernel, tg.grid(), dim3(B), 0, st, ws.recv_pos,
+                             reinterpret_cast<const uint4*>(recv), reinterpret_cast<const HandleRecord*>(ws.recv_meta),
+                             L, d.k, d.T, B, tg.groups, tg.slices, tg.tpb_log2, tg.m_log2,
+                             reinterpret_cast<uint4*>(out), ws.rank_recv_off, d.P, d.E, d.Ep);
     }
     const bool nt = streaming(d, d.Na * (16LL * L + 4LL * d.scales + 2LL * d.H));
     // streaming: e4m3 rows load and store nontemporally (stub 224 -> 231 us but the reverse exchange
@@ -121,9 +124,9 @@ hipError_t launch_stub(const Dims& d, const Workspace& ws, const void* recv, con
                         : (nt ? stub_kernel<false, false, true> : stub_kernel<false, false, false>);
     const int Bs = nt ? kStreamBlock : B;
     const int ss = (L + Bs - 1) / Bs;
-    return launch_kernel(kernel, row_grid(d.Na, ss), dim3(Bs), 0, st, reinterpret_cast<const uint4*>(recv), recv_scales,
-                  reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off, reinterpret_cast<uint4*>(out),
-                  d.P, d.E, d.Ep, L, ss);
+    return launch_kernel(kernel, row_grid(d.Na, ss), dim3(Bs), 0, st, reinterpret_cast<const uint4*>(recv),
+                         reinterpret_cast<const HandleRecord*>(ws.recv_meta), ws.rank_recv_off,
+                         reinterpret_cast<uint4*>(out), d.P, d.E, d.Ep, L, ss, Bs, recv_scales);
 }
 
 }  // namespace moe

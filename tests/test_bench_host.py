@@ -64,10 +64,9 @@ def test_byte_model_example_payload():
     ("void moe::(anonymous namespace)::count_pack_kernel<true, true, 16, 2, true>(x)", "count_pack_direct"),
     ("moe::(anonymous namespace)::pack_kernel<true, true, false, false>(x)", "pack"),
     ("moe::(anonymous namespace)::pack_kernel<false, false, false, true>(x)", "pack_direct"),
-    ("reduce_kernel<true, true, true, false>(x)", "reduce_direct"),
-    ("reduce_kernel<false, false, false, false>(x)", "reduce"),
-    ("reduce_kernel<false, false, true, true>(x)", "reduce_direct"), ("reduce_kernel<false, false, false, true>(x)",
-                                                                      "reduce"),
+    ("reduce_kernel<true, true, true>(x)", "reduce_direct"),
+    ("reduce_kernel<false, false, false>(x)", "reduce"),
+    ("reduce_affine_kernel<true>(x)", "reduce_direct"), ("reduce_affine_kernel<false>(x)", "reduce"),
     ("reverse_exchange_affine_kernel(x)", "reverse_exchange"), ("exchange_affine_kernel(x)", "exchange"),
     ("stub_affine_kernel(x)", "stub"),
     ("reverse_exchange_gather_kernel(x)", "reverse_exchange"), ("reverse_exchange_scatter_kernel(x)",
