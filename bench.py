@@ -520,6 +520,49 @@ def _counters_by(d: str, key) -> dict:
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
 
 
+def summarize_ceilings(bench_json: str) -> str:
+    """Markdown summary of the ceilings_tbps block of a bench.py output line (the default run, or --ceilings)."""
+    line = [x for x in open(bench_json).read().splitlines() if x.startswith("{")][-1]
+    c = json.loads(line)["ceilings_tbps"]
+    sizes = [label for label, _, _ in CEILING_SIZES]
+    moved = 91.8e6
+    out = ["# Probe ceilings: plain copy, streaming read, and four dependent copies of the decode bytes", "",
+           "Kernels: `probe_copy_kernel<policy>`, `probe_read_kernel<nontemporal>` and `probe_gather_kernel<policy>` in "
+           "`combine_router_softmax_expert_amd/csrc/probe.hip`, built like the path's kernels (kernel arguments "
+           "preloaded). Copy and read: one 16-byte unit per lane, consecutive lanes on consecutive units, 256-thread "
+           "workgroups (the row kernels' access pattern without the permutation). Gather: destination row r takes "
+           "source row perm[r], one unit per lane, the slices of a row adjacent (the streaming exchange's pattern).", "",
+           "Commands (from the repository root, on one MI355X):", "", "```",
+           "python3 bench.py --ceilings > <json>        # or the default python3 bench.py line",
+           "python3 bench.py --summarize-ceilings <json>", "```", "",
+           "Every figure is the mean of launches the GPU runs back to back: the host enqueues them behind a GPU spin, "
+           "so its pace does not enter.", "",
+           "TB/s of bytes moved (a copy moves twice its size); 10 launches at 1 GiB and 940 MB, 50 at 117 MB, 500 at "
+           "14.7 MB:", "",
+           "| size | copy, temporal | copy, nontemporal | copy, write-through stores | read, temporal | read, nontemporal |",
+           "|---|---|---|---|---|---|"]
+    for sz in sizes:
+        out.append(f"| {sz} | {c['copy_temporal_' + sz]} | {c['copy_nt_' + sz]} | {c['copy_write_through_' + sz]} | "
+                   f"{c['read_temporal_' + sz]} | {c['read_nt_' + sz]} |")
+    out += ["", "Four dependent copies that move the decode workload's dispatch+combine bytes (8.27, 14.68, 14.68 and "
+            "8.26 MB copied, 91.8 MB moved in all; each copy reads the buffer the copy before it wrote into), 500 "
+            "repetitions:", "", "| copies | store policy | us per four copies | of 8 TB/s |", "|---|---|---|---|"]
+    names = (("temporal", "write-back"), ("nt", "nontemporal"), ("write_through", "write-through"))
+    for tag, name in names:
+        us = c[f"decode_dc_four_copies_{tag}_us"]
+        out.append(f"| flat, contiguous | {name} | {us} | {moved / (us * 1e-6) / 8e12:.3f} |")
+    us = c["decode_dc_four_row_copies_identity_write_through_us"]
+    out.append(f"| rows of 14 KiB, identity order | write-through | {us} | {moved / (us * 1e-6) / 8e12:.3f} |")
+    for tag, name in names:
+        us = c[f"decode_dc_four_row_copies_permuted_{tag}_us"]
+        out.append(f"| rows of 14 KiB, random permutation | {name} | {us} | {moved / (us * 1e-6) / 8e12:.3f} |")
+    out += ["", "The row copies move 577, 1,024, 1,024 and 576 rows of 14 KiB; each takes its rows through a seeded "
+            "random permutation of the 1,024 rows of the buffer the copy before it wrote into (a row is read on another "
+            "XCD than the one that wrote it 7 times in 8, as in the path), or through the identity, which keeps each "
+            "row on its writer's XCD.", ""]
+    return "\n".join(out)
+
+
 def summarize_counters(config: str, path_dirs: list, probe_dirs: list) -> str:
     """Markdown table of the cache, latency and occupancy counters (COUNTER_PASSES) of the path's kernels,
     next to the probe copies and reads of the same sizes, per dispatch."""
@@ -828,6 +871,8 @@ def main():
     ap.add_argument("--trace-command", default="", help="command recorded with --summarize-trace")
     ap.add_argument("--summarize-traffic", action="store_true",
                     help="print the markdown summary of profiles/traffic.json for --config")
+    ap.add_argument("--summarize-ceilings", metavar="BENCH_JSON",
+                    help="print the markdown summary of the ceilings in a bench.py output (default run or --ceilings)")
     ap.add_argument("--summarize-counters", nargs=6, metavar=("L2", "LAT", "OCC", "L2_PROBE", "LAT_PROBE", "OCC_PROBE"),
                     help="print the markdown summary of the cache, latency and occupancy counter passes")
     args = ap.parse_args()
@@ -838,6 +883,10 @@ def main():
     if args.summarize_traffic:
         print(summarize_traffic(args.config))
         return
+    if args.summarize_ceilings:
+        print(summarize_ceilings(args.summarize_ceilings))
+        return
+
     if args.summarize_counters:
         print(summarize_counters(args.config, list(args.summarize_counters[:3]), list(args.summarize_counters[3:])))
         return
