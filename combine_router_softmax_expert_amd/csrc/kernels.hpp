@@ -172,9 +172,10 @@ inline dim3 row_grid(long long rows, int slices) { return dim3((unsigned)(rows *
 // in SGPRs (16 user SGPRs less the kernarg segment pointer), and the rest, the
 // hidden ones (workgroup size, grid size) included, come from a scalar load.
 // So the path's kernels list first the arguments their first loads depend on,
-// take their workgroup size as an argument (bs, equal to blockDim.x) instead of
-// reading the hidden one, and take no aggregate arguments (an aggregate ends the
-// preloaded ones).  Measured on gfx950 at 128 tokens x top-8 x 7168: whole step
+// take their workgroup size as an argument (bs, equal to blockDim.x) where the
+// hidden one would fall past the preloaded dwords (kernels with at most 10
+// dwords of arguments, such as the router and the reverse exchange, still read
+// it), and take no aggregate arguments (an aggregate ends the preloaded ones).  Measured on gfx950 at 128 tokens x top-8 x 7168: whole step
 // 29.57 -> 28.52 us, dispatch + combine 20.48 -> 19.89 us.
 
 // Threads per block of the streaming (nontemporal) exchange, reverse exchange
