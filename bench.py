@@ -808,16 +808,22 @@ def micro_batch_figures(r: "Runner", steps: int, parts: int = 2) -> dict:
         cc = B.Context(w.num_ranks, w.tokens_per_rank // parts, w.num_experts, w.top_k, w.hidden, fp8)
         mb.append((cc, cc.allocate(r.dev), r.x[rows].contiguous(), r.logits[rows].contiguous()))
     comm, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    fork, join = B.OrderEvent(), [B.OrderEvent(), B.OrderEvent()]
 
     def schedule(same_stream):
         cs = comm if same_stream else compute
 
-        def go():
-            comm.wait_stream(r.stream)
-            cs.wait_stream(r.stream)
+        def go():                  # the schedule between the launch stream's work before and after it
+            fork.record(r.stream)
+            fork.wait(comm)
+            if not same_stream:
+                fork.wait(cs)
             B.run_overlapped(mb, comm, cs)
-            r.stream.wait_stream(comm)
-            r.stream.wait_stream(cs)
+            join[0].record(comm)
+            join[0].wait(r.stream)
+            if not same_stream:
+                join[1].record(cs)
+                join[1].wait(r.stream)
         return go
 
     two, one = schedule(False), schedule(True)

@@ -83,6 +83,10 @@ def _load():
         "moe_probe_copy": (I32, [P, P, SZ, I32, P]),
         "moe_probe_read": (I32, [P, SZ, P, I32, P]),
         "moe_probe_gather": (I32, [P, I32, P, P, I32, I32, I32, P]),
+        "moe_event_create": (I32, [ctypes.POINTER(ctypes.c_void_p)]),
+        "moe_event_destroy": (I32, [P]),
+        "moe_event_record": (I32, [P, P]),
+        "moe_stream_wait_event": (I32, [P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_begin": (I32, [P]),
@@ -516,43 +520,79 @@ def _capturing(streams) -> bool:
     return False
 
 
+class OrderEvent:
+    """A library event for ordering two streams of one device (moe_event_*): no timing, no system-scope fence."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib.moe_event_create(ctypes.byref(h)), "moe_event_create")
+        self.handle = h
+
+    def record(self, stream=None):
+        _check(lib.moe_event_record(self.handle, _stream(stream)), "moe_event_record")
+
+    def wait(self, stream=None):
+        """Work enqueued on stream from now on waits for this event's latest record."""
+        _check(lib.moe_stream_wait_event(_stream(stream), self.handle), "moe_stream_wait_event")
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None and lib is not None:
+            lib.moe_event_destroy(self.handle)
+            self.handle = None
+
+
+_order_events = {}   # per device, reused by run_overlapped: a wait refers to the record enqueued before it
+
+
+def _order_event(device: int, i: int) -> OrderEvent:
+    import torch
+    pool = _order_events.setdefault(device, [])
+    while len(pool) <= i:
+        with torch.cuda.device(device):      # an event belongs to the device current at its creation
+            pool.append(OrderEvent())
+    return pool[i]
+
+
 def run_overlapped(parts, comm_stream, compute_stream):
     """Micro-batches through the split phases on two streams.
 
     ``parts`` is a list of (ctx, bufs, x, logits), one independent problem per
     micro-batch.  Routing, both dispatch halves and both combine halves run on
-    ``comm_stream``, the expert stage on ``compute_stream``; events order each
-    micro-batch's stages, so the expert stage of micro-batch i can overlap the
-    dispatch of i+1 and the combine of i-1 ([PPLX]: send and receive halves let
-    other work run in between).  Only launches and events: the caller
-    synchronises before reading the outputs.  Returns the handles.
+    ``comm_stream``, the expert stage on ``compute_stream``; library events
+    (OrderEvent: no timing, no system-scope fence) order each micro-batch's
+    stages, so the expert stage of micro-batch i can overlap the dispatch of i+1
+    and the combine of i-1 ([PPLX]: send and receive halves let other work run
+    in between).  With one stream for both, stream order alone orders them and no
+    event is recorded.  Only launches and events: the caller orders its own
+    streams around the schedule and synchronises before reading the outputs.
+    Returns the handles.
 
     Refuses graph capture (RuntimeError, before anything is enqueued): the schedule
-    records and waits on events it creates per call and drops when it returns, and
-    it does not fork from or join back into a capturing origin stream, which a
-    multi-stream capture needs."""
-    import torch
+    neither forks from nor joins back into a capturing origin stream, which a
+    multi-stream capture needs, and the library's events refuse capturing streams."""
     if _capturing((comm_stream, compute_stream)):
         raise RuntimeError("run_overlapped: a stream is capturing a graph; the two-stream schedule is not built "
-                           "for capture (its events live for one call and it does not join the capturing stream)")
-    handles, dispatched, computed = [], [], []
-    for ctx, bufs, x, logits in parts:
+                           "for capture (it neither forks from nor joins the capturing stream)")
+    handles = []
+    two = comm_stream.cuda_stream != compute_stream.cuda_stream
+    dev = comm_stream.device.index
+    for i, (ctx, bufs, x, logits) in enumerate(parts):
         moe_route_topk(ctx, logits, bufs["topk_ids"], bufs["topk_w"], comm_stream)
         h = moe_dispatch_send(ctx, x, bufs["topk_ids"], bufs["topk_w"], bufs["workspace"], bufs["send"],
                               bufs["send_scales"], comm_stream)
         moe_dispatch_recv(ctx, h, bufs["send"], bufs["send_scales"], bufs["recv"], bufs["recv_scales"], comm_stream)
-        ev = torch.cuda.Event()
-        ev.record(comm_stream)
         handles.append(h)
-        dispatched.append(ev)
-    for (ctx, bufs, _, _), h, ev in zip(parts, handles, dispatched):
-        compute_stream.wait_event(ev)
+        if two:
+            _order_event(dev, 2 * i).record(comm_stream)             # micro-batch i dispatched
+    for i, ((ctx, bufs, _, _), h) in enumerate(zip(parts, handles)):
+        if two:
+            _order_event(dev, 2 * i).wait(compute_stream)
         moe_expert_stub(ctx, h, bufs["recv"], bufs["recv_scales"], bufs["expert_out"], compute_stream)
-        done = torch.cuda.Event()
-        done.record(compute_stream)
-        computed.append(done)
-    for (ctx, bufs, _, _), h, ev in zip(parts, handles, computed):
-        comm_stream.wait_event(ev)
+        if two:
+            _order_event(dev, 2 * i + 1).record(compute_stream)      # micro-batch i's expert stage done
+    for i, ((ctx, bufs, _, _), h) in enumerate(zip(parts, handles)):
+        if two:
+            _order_event(dev, 2 * i + 1).wait(comm_stream)
         moe_combine_send(ctx, h, bufs["expert_out"], bufs["comb"], comm_stream)
         moe_combine_recv(ctx, h, bufs["comb"], bufs["topk_w"], bufs["y"], comm_stream)
     return handles

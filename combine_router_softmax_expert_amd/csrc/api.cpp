@@ -656,6 +656,56 @@ moe_status moe_combine_direct(moe_ctx* ctx, const moe_handle* handle, const uint
     });
 }
 
+moe_status moe_event_create(void** event) {
+    const CallScope scope("moe_event_create");
+    if (!event) return fail(MOE_ERR_INVALID_ARG, "event is NULL");
+    hipEvent_t ev = nullptr;
+    if (hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence); e != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+    *event = ev;
+    return MOE_OK;
+}
+
+moe_status moe_event_destroy(void* event) {
+    const CallScope scope("moe_event_destroy");
+    if (!event) return MOE_OK;
+    hipError_t e = hipEventDestroy(static_cast<hipEvent_t>(event));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "hipEventDestroy");
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status refuse_capture(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipError_t e = hipStreamIsCapturing(st, &cs); e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone) return fail(MOE_ERR_UNSUPPORTED, "the stream is capturing a graph");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_event_record(void* event, void* stream) {
+    const CallScope scope("moe_event_record");
+    if (!event) return fail(MOE_ERR_INVALID_ARG, "event is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (moe_status s = refuse_capture(st); s != MOE_OK) return s;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(event), st);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "hipEventRecord");
+}
+
+moe_status moe_stream_wait_event(void* stream, void* event) {
+    const CallScope scope("moe_stream_wait_event");
+    if (!event) return fail(MOE_ERR_INVALID_ARG, "event is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (moe_status s = refuse_capture(st); s != MOE_OK) return s;
+    hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(event), 0);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "hipStreamWaitEvent");
+}
+
 moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, int32_t policy, void* stream) {
     const CallScope scope("moe_probe_copy");
     if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src or dst is NULL");

@@ -309,6 +309,25 @@ moe_status moe_combine_send(moe_ctx* ctx, const moe_handle* handle, const uint16
 moe_status moe_combine_recv(moe_ctx* ctx, const moe_handle* handle, const uint16_t* comb_buf, const float* topk_w,
                             uint16_t* y, void* stream);
 
+/* Events for ordering the split phases across two streams of one device: record
+ * one on a stream after a half, wait for it on another stream before the next.
+ * They are HIP events created without timing and without the system-scope fence:
+ * the ordered work is on the same device, where each kernel's own release and
+ * acquire make its stores visible, so a record-and-wait pair costs less than
+ * with a default event.  A wait refers to the latest record enqueued before
+ * it, so an event can be recorded again once its wait is enqueued.
+ *   moe_event_create   a new event on the current device, in *event
+ *   moe_event_destroy  destroys it (NULL: nothing)
+ *   moe_event_record   records event on stream (NULL: the null stream)
+ *   moe_stream_wait_event  work enqueued on stream after this call waits for the
+ *                      event's latest record
+ * MOE_ERR_INVALID_ARG for a NULL event (or out pointer), MOE_ERR_UNSUPPORTED
+ * while the stream is capturing a graph, MOE_ERR_HIP if a HIP call fails. */
+moe_status moe_event_create(void** event);
+moe_status moe_event_destroy(void* event);
+moe_status moe_event_record(void* event, void* stream);
+moe_status moe_stream_wait_event(void* stream, void* event);
+
 /* ---- measurement aids (not part of the path) ------------------------------- */
 
 /* Ceilings of this GPU for the row kernels' access pattern ([A2A] 11.2: read a

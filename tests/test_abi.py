@@ -271,6 +271,14 @@ def test_probes_validate_arguments(b):
     assert G(fake, 4, fake, fake, 0, 64, 1, None) == 0              # no rows: nothing enqueued
 
 
+def test_order_events_validate_arguments(b):
+    assert b.lib.moe_event_create(None) == -1                 # nowhere to return the event
+    assert b.lib.moe_event_destroy(None) == 0                 # nothing to destroy
+    assert b.lib.moe_event_record(None, None) == -1
+    assert b"event is NULL" in b.lib.moe_last_error()
+    assert b.lib.moe_stream_wait_event(None, None) == -1
+
+
 def test_stale_and_foreign_handles(b):
     st, h = _create(b)
     st2, h2 = _create(b)

@@ -7,6 +7,8 @@ tokens (ids, integer parts, rows, scales, expert outputs and combine rows bit fo
 bit, weights and y to the parity tolerances), and routing, weights and y must also
 equal, bit for bit, what the whole batch gives for those tokens."""
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -63,9 +65,10 @@ def test_micro_batches_on_two_streams_match_the_oracle(orc, name, parts, same_st
 
 
 def test_run_overlapped_refuses_stream_capture():
-    """The micro-batch schedule forks work onto two streams with events it creates per call;
-    it is not built for graph capture, so it refuses to run while the caller's stream, or
-    either of its own, is capturing, before it enqueues anything."""
+    """The micro-batch schedule forks work onto two streams and orders them with the library's
+    events; it is not built for graph capture, so it refuses to run while the caller's stream,
+    or either of its own, is capturing, before it enqueues anything.  The events refuse a
+    capturing stream by themselves too."""
     import torch
     from combine_router_softmax_expert_amd import binding as B
 
@@ -86,6 +89,10 @@ def test_run_overlapped_refuses_stream_capture():
             counter.add_(1.0)           # one captured node, so the graph is not empty
             with pytest.raises(RuntimeError, match="capturing"):
                 B.run_overlapped([(ctx, bufs, x, logits)], comm, compute)
+            ev = B.OrderEvent()
+            assert B.lib.moe_event_record(ev.handle, ctypes.c_void_p(side.cuda_stream)) == -2
+            assert b"capturing" in B.lib.moe_last_error()
+            assert B.lib.moe_stream_wait_event(ctypes.c_void_p(side.cuda_stream), ev.handle) == -2
         finally:
             graph.capture_end()
     torch.cuda.synchronize()
@@ -93,3 +100,27 @@ def test_run_overlapped_refuses_stream_capture():
     torch.cuda.synchronize()
     assert counter.item() == 1.0        # the capture holds the add alone: nothing of the schedule ran or was captured
     del graph
+
+
+def test_order_event_orders_two_streams():
+    """Work enqueued on a stream after OrderEvent.wait starts only after the work the other stream had
+    enqueued before OrderEvent.record: a copy on the waiting stream reads what a kernel on the recording
+    stream wrote after a long GPU spin (without the wait it would read the old contents), on every one of
+    several rounds that reuse the same event."""
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = B.OrderEvent()
+    src = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    for r in range(1, 4):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(a):
+            torch.cuda._sleep(20_000_000)         # a few milliseconds of spinning on stream a
+            src.fill_(r)
+        ev.record(a)
+        ev.wait(b)
+        with torch.cuda.stream(b):
+            dst = src.clone()
+        torch.cuda.synchronize()
+        assert bool((dst == r).all()), f"round {r}: the copy did not wait for the fill"
