@@ -250,14 +250,9 @@ hipError_t launch_reverse_exchange(const Dims& d, const Workspace& ws, const uin
                              reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb), ws.recv_pos, L,
                              sr);
     }
-    // rows longer than 512 units in 512-thread workgroups, the second slice partly idle (measured on gfx950
-    // at 2048 tokens x top-2 x 7168: 16.57 -> 15.63 us against two 448-thread slices; 128 tokens x top-8
-    // unchanged; 256 and 192 threads slower)
-    const int Bs = L > 512 ? 512 : B;
-    const int ss = (L + Bs - 1) / Bs;
-    return launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, ss), dim3(Bs), 0, st,
+    return launch_kernel(reverse_exchange_scatter_kernel, row_grid(d.Na, slices), dim3(B), 0, st,
                          reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(comb),
-                         reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, ss);
+                         reinterpret_cast<const HandleRecord*>(ws.recv_meta), d.Tp, d.k, L, slices);
 }
 
 }  // namespace moe
