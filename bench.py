@@ -796,8 +796,9 @@ def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_fo
 
 def micro_batch_figures(r: "Runner", steps: int, parts: int = 2) -> dict:
     """Micro-batches through the split phases: the expert stage of one on a second stream overlaps the
-    dispatch and combine of the others.  Wall time on two streams and on one, eagerly and with the host
-    enqueued ahead (gated), against the sum of the schedule's kernel durations (the phases end to end)."""
+    dispatch and combine of the others, the streams ordered by the library's events.  Wall time on two
+    streams and on one (stream order alone, no events), eagerly and with the host enqueued ahead (gated),
+    against the sum of the schedule's kernel durations (the phases end to end)."""
     B, torch, w = r.B, r.torch, r.w
     from combine_router_softmax_expert_amd import workloads as wl
 
