@@ -175,8 +175,9 @@ inline dim3 row_grid(long long rows, int slices) { return dim3((unsigned)(rows *
 // take their workgroup size as an argument (bs, equal to blockDim.x) where the
 // hidden one would fall past the preloaded dwords (kernels with at most 10
 // dwords of arguments, such as the router and the reverse exchange, still read
-// it), and take no aggregate arguments (an aggregate ends the preloaded ones).  Measured on gfx950 at 128 tokens x top-8 x 7168: whole step
-// 29.57 -> 28.52 us, dispatch + combine 20.48 -> 19.89 us.
+// it), and take no aggregate arguments (an aggregate ends the preloaded ones).
+// Measured on gfx950 at 128 tokens x top-8 x 7168: whole step 29.57 -> 28.52
+// us, dispatch + combine 20.48 -> 19.89 us.
 
 // Threads per block of the streaming (nontemporal) exchange, reverse exchange
 // and expert stub: one wave, so a row takes L / 64 workgroups.  Measured on
