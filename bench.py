@@ -581,7 +581,8 @@ def summarize_counters(config: str, path_dirs: list, probe_dirs: list) -> str:
         label = {"0": "temporal", "1": "nontemporal", "2": "write-through", "false": "temporal",
                  "true": "nontemporal"}[pol]
         mb = int(r["Grid_Size"]) * 16 / 1e6
-        return f"probe {'copy' if 'copy' in n else 'read'} {mb:.1f} MB, {label}"
+        kind = "copy" if "probe_copy" in n else "row gather" if "probe_gather" in n else "read"
+        return f"probe {kind} {mb:.1f} MB, {label}"
 
     def merged(dirs, key):
         out = {}
