@@ -87,11 +87,12 @@ def logical_payload_bytes(w) -> int:
 
 
 def source_sha(kernel: str) -> str:
-    """Hash of what a kernel's machine code is built from: its source, the device helpers and the build
-    script with its compiler flags."""
+    """Hash of what a kernel's machine code is built from: its source, the device helpers, the launch
+    constants and shared layouts, and the build script with its compiler flags."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "combine_router_softmax_expert_amd")
-    for f in (os.path.join("csrc", KERNEL_SOURCES[kernel]), os.path.join("csrc", "device.hpp"), "_build.py"):
+    for f in (os.path.join("csrc", KERNEL_SOURCES[kernel]), os.path.join("csrc", "device.hpp"),
+              os.path.join("csrc", "kernels.hpp"), "_build.py"):
         with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -3,10 +3,11 @@
 Flags: -O3, IEEE fp32 division (hipcc's default; no fast-math), no implicit
 contraction into fused multiply-adds (the combine's FMAs are explicit),
 packed fp32 instructions disabled for all device code, and kernel arguments
-preloaded into SGPRs: gfx950 can start a wave with the first 16 dwords of its
-kernel arguments (hidden ones such as the workgroup size included, when they
-fit) already in SGPRs, so the wave skips the scalar load of its arguments before
-its first address computation.  The compiler keeps a prologue that loads them
+preloaded into SGPRs: gfx950 can start a wave with the first 14 dwords of its
+kernel arguments already in SGPRs (16 user SGPRs less the two that hold the
+kernel-argument pointer; the hidden ones, such as the workgroup size, count only
+when they fall within those 14), so the wave skips the scalar load of its
+arguments before its first address computation.  The compiler keeps a prologue that loads them
 for firmware that does not preload.  Measured on gfx950, whole step, two
 interleaved runs each: 128 tokens x top-8 x 7168 30.42 -> 29.54 us (dispatch +
 combine 21.10 -> 20.70 us); 2048 tokens x top-2 FP8 68.97 -> 68.10 us; 8192
