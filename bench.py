@@ -702,13 +702,23 @@ class Runner:
                 kt[name] = (a + launches, b + tot)
         return kt, ms
 
-    def flushed(self, fn, n):
-        """Median ms of n calls, each after a 1 GiB write that evicts the caches (Infinity Cache included)."""
+    def flushed(self, fn, n, evict="write"):
+        """Median ms of n single calls, each after an eviction pass on the launch stream:
+        "write" writes 1 GiB, which evicts the L2s and the 256 MB Infinity Cache and leaves the latter full of
+        dirty lines that the measured call's own misses then have to write back; "read" reads 1 GiB (temporal
+        loads), which evicts with clean lines; "none" runs no pass (the warm single-call time)."""
         torch, np = self.torch, self.np
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev) if evict != "none" else None
+        sink = torch.zeros(256, dtype=torch.int32, device=self.dev)
+        if flush is not None:
+            flush.fill_(1)
         times = []
         for _ in range(n):
-            flush.fill_(1)
+            if evict == "write":
+                with torch.cuda.stream(self.stream):
+                    flush.fill_(1)
+            elif evict == "read":
+                self.B.moe_probe_read(flush, sink, False, self.stream)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(self.stream)
             fn()
@@ -766,7 +776,9 @@ def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_fo
     trace_marker(r)                      # the per-kernel pass, bracketed for summarize_trace
     kt, ms_with_events = r.kernel_times(r.step, steps)
     trace_marker(r)
+    dc_single = r.flushed(r.dispatch_combine, flush_runs, "none") if flush_runs else None
     dc_flushed = r.flushed(r.dispatch_combine, flush_runs) if flush_runs else None
+    dc_flushed_clean = r.flushed(r.dispatch_combine, flush_runs, "read") if flush_runs else None
     other = not r.direct
     other_block = None
     if other_form:
@@ -786,7 +798,10 @@ def measure_core(r: "Runner", steps: int, flush_runs: int, config: str, other_fo
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(w.tokens / (ms_step * 1e-3), 1),
         "ms_per_step_gated": round(step_gated_ms, 5),
         "dispatch_combine": dict(dc_block(w, dc_ms, kb, kt), gated_ms=round(dc_gated_ms, 5)),
+        "dispatch_combine_single_call": None if dc_single is None else dc_block(w, dc_single, kb, kt),
         "dispatch_combine_cache_flushed": None if dc_flushed is None else dc_block(w, dc_flushed, kb, kt),
+        "dispatch_combine_cache_flushed_clean": None if dc_flushed_clean is None else dc_block(w, dc_flushed_clean,
+                                                                                              kb, kt),
         "other_mode_dispatch_combine": other_block,
         "kernels": per_kernel_table(kt, kb),
         "phases_ms": {k: round(v, 5) for k, v in phases.items()},
@@ -959,7 +974,7 @@ def main():
 
     core = measure_core(r, args.steps, 0 if args.core_only else flush_runs, args.config, other_form=extras)
     latency_ms = None
-    ag = graph = micro = cold_ms = None
+    ag = graph = micro = cold_ms = cold_clean_ms = None
     if extras:
         latency_ms = {"step": latency_percentiles(r.step, args.steps),
                       "dispatch_combine": latency_percentiles(r.dispatch_combine, args.steps)}
@@ -977,6 +992,7 @@ def main():
         r.step()   # leave the buffers as the measured form wrote them
         if flush_runs:
             cold_ms = r.flushed(r.step, flush_runs)
+            cold_clean_ms = r.flushed(r.step, flush_runs, "read")
 
         # the step captured once in a HIP graph and replayed (no per-call host work)
         def graph_ms(direct):
@@ -1031,7 +1047,9 @@ def main():
                                  logical_payload_bytes=logical_payload_bytes(w),
                                  logical_payload_gbps=round(logical_payload_bytes(w) / (core["dispatch_combine"]["ms"]
                                                                                         * 1e-3) / 1e9, 1)),
+        "dispatch_combine_single_call": core["dispatch_combine_single_call"],
         "dispatch_combine_cache_flushed": core["dispatch_combine_cache_flushed"],
+        "dispatch_combine_cache_flushed_clean": core["dispatch_combine_cache_flushed_clean"],
         "other_mode": core["other_mode_dispatch_combine"],
         "allgather_dispatch": ag,
         "graph_replay": graph,
@@ -1042,6 +1060,7 @@ def main():
         "latency_ms": latency_ms,
         "ms_per_step_with_kernel_events": core["ms_per_step_with_kernel_events"],
         "ms_per_step_cache_flushed": None if cold_ms is None else round(cold_ms, 5),
+        "ms_per_step_cache_flushed_clean": None if cold_clean_ms is None else round(cold_clean_ms, 5),
         "metadata_bytes_per_step": metadata_bytes(w),
         "roofline": core["roofline"],
         "h7168_workloads": None,
