@@ -703,15 +703,18 @@ class Runner:
         return kt, ms
 
     def flushed(self, fn, n, evict="write"):
-        """Median ms of n single calls, each after an eviction pass on the launch stream:
-        "write" writes 1 GiB, which evicts the L2s and the 256 MB Infinity Cache and leaves the latter full of
-        dirty lines that the measured call's own misses then have to write back; "read" reads 1 GiB (temporal
-        loads), which evicts with clean lines; "none" runs no pass (the warm single-call time)."""
+        """Median ms of n single calls, each after a pass on the launch stream that keeps the GPU busy while the
+        host enqueues the call (so the host's launch is not timed): "write" writes 1 GiB, which evicts the L2s
+        and the 256 MB Infinity Cache and leaves the latter full of dirty lines that the measured call's own
+        misses then have to write back; "read" reads 1 GiB (temporal loads), which evicts with clean lines;
+        "none" spins for 0.2 ms and touches no memory (the warm single-call time)."""
         torch, np = self.torch, self.np
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev) if evict != "none" else None
         sink = torch.zeros(256, dtype=torch.int32, device=self.dev)
         if flush is not None:
             flush.fill_(1)
+        elif self._cycles_per_ms is None:
+            self._cycles_per_ms = _spin_cycles_per_ms(self.stream)
         times = []
         for _ in range(n):
             if evict == "write":
@@ -719,6 +722,9 @@ class Runner:
                     flush.fill_(1)
             elif evict == "read":
                 self.B.moe_probe_read(flush, sink, False, self.stream)
+            else:
+                with torch.cuda.stream(self.stream):
+                    torch.cuda._sleep(int(0.2 * self._cycles_per_ms))
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(self.stream)
             fn()
