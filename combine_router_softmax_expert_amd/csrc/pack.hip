@@ -11,8 +11,10 @@
 // One token per workgroup slice: the token's row is read once (16-byte loads)
 // and written to its k send rows; the FP8 form is computed once per token and
 // copied k times.  FP8: a lane owns 16 channels, 8 lanes a 128-channel block;
-// amax by DPP moves within the 8 lanes, scale = amax / 448 (fp32 division), code =
-// e4m3(x / scale) (fp32 division, then v_cvt_pk_fp8_f32: nearest even).  The positions of the k
+// amax by DPP moves within the 8 lanes, scale = amax / 448 and code =
+// e4m3(x / scale), each quotient the correctly rounded fp32 one (for x / scale,
+// or one on the same side of every E4M3 rounding boundary; see store_rows),
+// encoded by v_cvt_pk_fp8_f32 (nearest even).  The positions of the k
 // assignments are send_off[s][e] + bucket rank and recv_off[s][e] + bucket
 // rank; the first slice also writes the handle record, the position arrays and
 // the send <-> receive maps that the exchange uses.  The direct form writes each
@@ -130,9 +132,10 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
         amax = max8(amax);
-        const float scale = amax / 448.0f;
+        float scale;
         uint32_t q[4];
         if (amax == 0.0f) {                       // all zeros: scale 0, codes keep each zero's sign
+            scale = 0.0f;
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
                 q[w4] = 0u;
@@ -140,24 +143,38 @@ __device__ __forceinline__ void store_rows(const uint4& xa, const uint4& xb, con
                 for (int i = 0; i < 4; ++i) q[w4] |= ((__float_as_uint(f[4 * w4 + i]) >> 24) & 0x80u) << (8 * i);
             }
         } else if (amax >= 0x1p-64f && amax < __builtin_inff()) {
+            // amax / 448 by a multiply with the rounded reciprocal of 448 and one
+            // correction with the exact remainder: equal to the correctly rounded
+            // quotient for every finite bf16 amax (checked exhaustively).
+            constexpr float kInv448 = 1.0f / 448.0f;
+            const float s0 = amax * kInv448;
+            scale = fmaf(fmaf(-s0, 448.0f, amax), kInv448, s0);
             // x / scale through the reciprocal: q0 = x * r, then one correction with the
             // exact remainder x - q0 * scale (an FMA).  The corrected quotient can be one
             // ulp off the correctly rounded one, but never across an E4M3 rounding
             // boundary: checked for every bf16 amax >= 2^-64 and every bf16 |x| <= amax
-            // (the remainder stays far from underflow there).  The sign is copied from
-            // x: for x = -0 the correction adds +0 to -0 and would give +0, where the
-            // quotient -0 / scale is -0 (code 0x80); every other quotient already has
-            // the sign of x.  Four operations per channel instead of a full division.
+            // (the remainder stays far from underflow there).  Three operations per
+            // channel instead of a full division.  Every quotient has the sign of its x
+            // but one: for x = -0 the correction adds +0 to -0 and gives +0, where
+            // -0 / scale is -0 (code 0x80).  Each code's sign bit is therefore ORed
+            // from its x: a byte permute gathers the high bytes of four bf16 values,
+            // whose top bits are their signs, into the four code bytes.
             const float r = 1.0f / scale;
             float v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float q0 = f[i] * r;
-                v[i] = __builtin_copysignf(fmaf(fmaf(-q0, scale, f[i]), r, q0), f[i]);
+                v[i] = fmaf(fmaf(-q0, scale, f[i]), r, q0);
             }
+            const uint32_t src[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) q[w4] = pack4_e4m3(v[4 * w4], v[4 * w4 + 1], v[4 * w4 + 2], v[4 * w4 + 3]);
-        } else {                                  // tiny blocks: correctly rounded division
+            for (int w4 = 0; w4 < 4; ++w4) {
+                q[w4] = pack4_e4m3(v[4 * w4], v[4 * w4 + 1], v[4 * w4 + 2], v[4 * w4 + 3]);
+                // bytes 1 and 3 of the word holding values 4 w4 and 4 w4 + 1, then of the next word
+                q[w4] |= __builtin_amdgcn_perm(src[2 * w4 + 1], src[2 * w4], 0x07050301u) & 0x80808080u;
+            }
+        } else {                                  // tiny or non-finite blocks: correctly rounded division
+            scale = amax / 448.0f;
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4)
                 q[w4] = pack4_e4m3(f[4 * w4] / scale, f[4 * w4 + 1] / scale, f[4 * w4 + 2] / scale,
@@ -450,10 +467,14 @@ __global__ __launch_bounds__(512) void count_pack_kernel(const uint4* __restrict
 // Dynamic LDS of the counting form: E 64-bit histogram entries and E + 1 prefix sums.
 static size_t count_pack_lds(int E) { return sizeof(uint64_t) * (size_t)E + sizeof(int32_t) * ((size_t)E + 1); }
 
-// Ids each thread of the counting form loads (unrolled, all in flight): 4, 8 or 16.
+// Ids each thread of the counting form loads (unrolled, all in flight): 4, 8, 12 or 16.
+// Every id slot beyond N_a still costs its clamped load and its range test, so the
+// count is rounded up to a multiple of 4 only (2048 tokens x top-2 over 448-thread
+// workgroups, 9.1 ids per thread: 12 against 16 took the counting pack from 11.03 to
+// 10.83 us on gfx950, bit-identical).
 int ids_per_thread(long long Na, int B) {
     const long long m = (Na + B - 1) / B;
-    return m <= 4 ? 4 : m <= 8 ? 8 : 16;
+    return m <= 4 ? 4 : m <= 8 ? 8 : m <= 12 ? 12 : 16;
 }
 
 // Tokens per workgroup of the counting form: more tokens share one counting
@@ -512,14 +533,17 @@ hipError_t launch_pack(const Dims& d, const uint16_t* x, const int32_t* ids, con
     if (pack_counts(d)) {
         const int mi = ids_per_thread(d.Na, B);
         const int tpb = tokens_per_block(d);
-        auto pick = [&](auto fp8, auto dir) {
+        auto by_tpb = [&](auto fp8, auto dir, auto m) {
             constexpr bool F = decltype(fp8)::value, D = decltype(dir)::value;
-            if (tpb == 4) return mi == 4 ? count_pack_kernel<F, D, 4, 4> : mi == 8 ? count_pack_kernel<F, D, 8, 4>
-                                                                                   : count_pack_kernel<F, D, 16, 4>;
-            if (tpb == 2) return mi == 4 ? count_pack_kernel<F, D, 4, 2> : mi == 8 ? count_pack_kernel<F, D, 8, 2>
-                                                                                   : count_pack_kernel<F, D, 16, 2>;
-            return mi == 4 ? count_pack_kernel<F, D, 4, 1> : mi == 8 ? count_pack_kernel<F, D, 8, 1>
-                                                                     : count_pack_kernel<F, D, 16, 1>;
+            constexpr int MI = decltype(m)::value;
+            return tpb == 4 ? count_pack_kernel<F, D, MI, 4> : tpb == 2 ? count_pack_kernel<F, D, MI, 2>
+                                                                        : count_pack_kernel<F, D, MI, 1>;
+        };
+        auto pick = [&](auto fp8, auto dir) {
+            return mi == 4    ? by_tpb(fp8, dir, std::integral_constant<int, 4>{})
+                   : mi == 8  ? by_tpb(fp8, dir, std::integral_constant<int, 8>{})
+                   : mi == 12 ? by_tpb(fp8, dir, std::integral_constant<int, 12>{})
+                              : by_tpb(fp8, dir, std::integral_constant<int, 16>{});
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
@@ -558,8 +582,10 @@ hipError_t launch_pack_handles(const Dims& d, const int32_t* ids, const float* w
             return tpb == 4 ? count_pack_kernel<false, true, MI, 4, false>
                  : tpb == 2 ? count_pack_kernel<false, true, MI, 2, false> : count_pack_kernel<false, true, MI, 1, false>;
         };
-        auto kernel = mi == 4 ? pick(std::integral_constant<int, 4>{})
-                    : mi == 8 ? pick(std::integral_constant<int, 8>{}) : pick(std::integral_constant<int, 16>{});
+        auto kernel = mi == 4    ? pick(std::integral_constant<int, 4>{})
+                      : mi == 8  ? pick(std::integral_constant<int, 8>{})
+                      : mi == 12 ? pick(std::integral_constant<int, 12>{})
+                                 : pick(std::integral_constant<int, 16>{});
         const size_t lds = count_pack_lds(d.E);
         const unsigned blocks = (unsigned)(d.P + (d.T + tpb - 1) / tpb);
         return launch_kernel(kernel, row_grid(blocks, 1), dim3(B), lds, st, static_cast<const uint4*>(nullptr), ids, w,
