@@ -196,6 +196,57 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
                       "copy_tbps": round(2 * nbytes / (ms * 1e-3) / 1e12, 3)}))
 
 
+def eviction_probe(dev, stream, nbytes: int = 117_440_512, reps: int = 20) -> dict:
+    """Median µs of single 117 MB probe reads and copies (moe_probe_read / moe_probe_copy, temporal), each after
+    one pass on the launch stream: none (the host's launch is timed too), a 0.2 ms GPU spin (warm), a 1 GiB write
+    (evicts the caches and leaves the Infinity Cache full of dirty lines), a 1 GiB temporal read (evicts with
+    clean lines), a 1 GiB nontemporal read, and the write followed by the read.  It separates what a cold cache
+    costs a call from what the write-back of a flush's own dirty lines costs it."""
+    import numpy as np
+    import torch
+
+    from combine_router_softmax_expert_amd import binding as B
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cyc = _spin_cycles_per_ms(stream)
+
+    def fill():
+        with torch.cuda.stream(stream):
+            flush.fill_(1)
+
+    def spin():
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(0.2 * cyc))
+
+    passes = {
+        "none": lambda: None,
+        "spin_0.2ms": spin,
+        "write_1GiB": fill,
+        "read_1GiB": lambda: B.moe_probe_read(flush, sink, False, stream),
+        "read_nt_1GiB": lambda: B.moe_probe_read(flush, sink, True, stream),
+        "write_then_read_1GiB": lambda: (fill(), B.moe_probe_read(flush, sink, False, stream)),
+    }
+    ops = {"read_117MB": lambda: B.moe_probe_read(src, sink, False, stream),
+           "copy_117MB": lambda: B.moe_probe_copy(src, dst, 0, stream)}
+    out = {}
+    for op_name, op in ops.items():
+        op()
+        for name, pre in passes.items():
+            times = []
+            for _ in range(reps):
+                pre()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                op()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1e3)
+            out.setdefault(op_name, {})[name] = round(float(np.median(times)), 2)
+    return {"eviction_probe_us": out, "reps": reps, "bytes": nbytes}
+
+
 CEILING_SIZES = (("1GiB", 1 << 30, 10), ("940MB", 939_524_096, 10), ("117MB", 117_440_512, 50),
                  ("14.7MB", 14_680_064, 500))
 
@@ -891,6 +942,8 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only run the copy and streaming-read probes and print their rates")
+    ap.add_argument("--eviction-probe", action="store_true",
+                    help="only time single 117 MB probe reads and copies after each cache-eviction pass")
     ap.add_argument("--reps-scale", type=float, default=1.0,
                     help="scale the probes' repetitions (short runs under a counter profiler)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -932,6 +985,12 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.eviction_probe:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(eviction_probe(torch.device("cuda:0"), torch.cuda.current_stream())), flush=True)
         return
 
     if args.ceilings:
