@@ -106,6 +106,29 @@ __device__ __forceinline__ void st16_row(uint4* base, int row, int units, int u,
     }
 }
 
+// Write-through store (the device-scope cache policy, SC1, as st16_row) of
+// element i of row `row` of an array of rows of `count` 4- or 16-byte elements,
+// for the small per-row arrays (FP8 scales, handle records) that a kernel writes
+// beside its write-through rows and the next kernel reads from other XCDs.  The
+// row must be the same in every active lane; the buffer's record count is the
+// row's bytes, so the hardware drops any store past the row.
+template <typename T>
+__device__ __forceinline__ void st_through_row(T* base, int row, int count, int i, const T& v) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 16, "4- or 16-byte elements");
+    const int r = __builtin_amdgcn_readfirstlane(row);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base + (size_t)r * count, (short)0,
+                                                                          count * (int)sizeof(T), kRawBufferWord3);
+    if constexpr (sizeof(T) == 4) {
+        uint32_t w;
+        __builtin_memcpy(&w, &v, 4);
+        __builtin_amdgcn_raw_buffer_store_b32(w, rsrc, i * 4, 0, kStoreDeviceScope);
+    } else {
+        u32x4_t w;
+        __builtin_memcpy(&w, &v, 16);
+        __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, i * 16, 0, kStoreDeviceScope);
+    }
+}
+
 // ---- OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 significand bits,
 // largest finite 448, NaN = S.1111.111, no infinities) ------------------------------
 // gfx950's v_cvt_pk_fp8_f32 / v_cvt_pk_f32_fp8 work in this format with round
