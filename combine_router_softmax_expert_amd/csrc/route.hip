@@ -25,7 +25,10 @@
 // exp(l_j - l_max) / sum_sel exp(l_i - l_max): the full partition function
 // cancels.  Those k exponentials (evaluated together, one per lane, after the
 // selection) and the slot-order sum run in double, so the fp32 weights are the
-// correctly rounded ones up to a double ulp.
+// correctly rounded ones up to a double ulp.  The ids and weights are written
+// through (st_through_row): every workgroup of the counting pack reads all of
+// them next, from every XCD (whole step at 128 tokens x top-8 x 7168 on gfx950:
+// 28.30 -> 28.06 us, the router 4.04 -> 3.80 us).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -95,9 +98,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     const double my_e = gl < k ? exp(my_l - m) : 0.0;
     double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += __shfl(my_e, j, G);
-    if (valid && gl < k) {
-        ids[(size_t)t * k + gl] = my_id;
-        w[(size_t)t * k + gl] = nan_seen ? __int_as_float(0x7FC00000) : (float)(my_e / sum);
+    if (valid && gl < k) {   // the wave's tokens are consecutive: one row of kTokensPerWave * k entries
+        const int i = (lane / G) * k + gl;
+        st_through_row(ids, wave, kTokensPerWave * k, i, my_id);
+        st_through_row(w, wave, kTokensPerWave * k, i, nan_seen ? __int_as_float(0x7FC00000) : (float)(my_e / sum));
     }
 }
 
@@ -180,8 +184,8 @@ __global__ __launch_bounds__(256) void route_topk_wave_kernel(const float* __res
     double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += readlane_f64(my_e, j);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_id;
-        w[(size_t)t * k + lane] = row_nan ? nan : (float)(my_e / sum);
+        st_through_row(ids, t, k, lane, my_id);
+        st_through_row(w, t, k, lane, row_nan ? nan : (float)(my_e / sum));
     }
 }
 
