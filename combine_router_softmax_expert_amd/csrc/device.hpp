@@ -14,12 +14,14 @@ constexpr int kFp8Block = 128;   // channels per FP8 scale, per token
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// Two fp32 values -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950),
-// `lo` in bits 0..15.
+// Two fp32 values -> two bf16 (round to nearest even), `lo` in bits 0..15: one
+// v_cvt_pk_bf16_f32 on gfx950.  Converted one by one, each value took its own
+// conversion and the pair a shift and an OR to pack.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // 8 bf16 in a 16-byte vector -> 8 fp32
