@@ -116,7 +116,8 @@ def load_traffic(config: str, kernel: str):
 # the direct form (None: the kernel has no direct form of its own)
 KERNEL_NAME_PATTERNS = (
     ("route_topk", "route_topk", None), ("count_scan_single_kernel", "count", None), ("count_kernel", "count", None),
-    ("scan_kernel", "scan", None), ("count_pack_kernel", "count_pack", 1), ("pack_kernel", "pack", 3),
+    ("scan_kernel", "scan", None), ("scan_spread_kernel", "scan", None), ("count_pack_kernel", "count_pack", 1),
+    ("pack_kernel", "pack", 3),
     ("allgather_kernel", "allgather", None), ("handle_kernel", "handles", None), ("select_kernel", "select", None),
     ("select_scatter_kernel", "select", None), ("reverse_exchange_", "reverse_exchange", None),
     ("exchange_kernel", "exchange", None), ("exchange_affine_kernel", "exchange", None), ("stub_kernel", "stub", None),

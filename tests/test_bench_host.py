@@ -72,6 +72,7 @@ def test_byte_model_example_payload():
     ("reverse_exchange_gather_kernel(x)", "reverse_exchange"), ("reverse_exchange_scatter_kernel(x)",
                                                                 "reverse_exchange"),
     ("exchange_kernel<true>(x)", "exchange"), ("count_scan_single_kernel(x)", "count"), ("scan_kernel(x)", "scan"),
+    ("scan_spread_kernel(x)", "scan"),
     ("allgather_kernel<true, false, false>(x)", "allgather"), ("select_scatter_kernel<false>(x)", "select"),
     ("select_kernel<true>(x)", "select"), ("handle_kernel(x)", "handles"),
     ("count_pack_kernel<false, true, 8, 1, false>(x)", "count_handles"),
