@@ -291,7 +291,8 @@ def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
     Rates in TB/s of bytes moved (a copy moves 2x its size).  Each figure is the mean of launches the GPU
     runs back to back (enqueued behind a GPU spin, so the host's pace does not enter).  Then four dependent
     copies that move the decode workload's dispatch+combine bytes: contiguous, and as row gathers through a
-    random permutation or the identity (microseconds per four copies)."""
+    random permutation or the identity (microseconds per four copies); and the skewed workload's streaming row
+    gather (65,536 rows of 14 KiB through a random permutation or the identity, TB/s)."""
     import torch
 
     from combine_router_softmax_expert_amd import binding as B
@@ -361,6 +362,22 @@ def ceilings(dev, stream, reps_scale: float = 1.0) -> dict:
             us = gated_ms(chain, max(2, int(500 * reps_scale)), stream, cpm, chunk=25) * 1e3
             out[f"decode_dc_four_row_copies_{order}_{tag}_us"] = round(us, 3)
     del rbufs, perms
+    # the skewed workload's row gather: 65,536 rows of 14 KiB (940 MB), nontemporal, each destination row read
+    # from a source row through a seeded random permutation (the streaming reverse exchange's pattern), and
+    # through the identity (a plain row copy of the same shape); TB/s of bytes moved
+    w5 = wl.WORKLOADS["c5"]
+    n5, row5 = w5.tokens * w5.top_k, 2 * w5.hidden
+    src5 = torch.zeros((n5, row5), dtype=torch.uint8, device=dev)
+    dst5 = torch.empty_like(src5)
+    perm5 = {"permuted": torch.from_numpy(np.random.default_rng(21).permutation(n5).astype(np.int32)).to(dev),
+             "identity": torch.arange(n5, dtype=torch.int32, device=dev)}
+    for order, perm in perm5.items():
+        def gather():
+            B.moe_probe_gather(src5, dst5, perm, B.PROBE_NONTEMPORAL, stream)
+        gather()
+        ms = gated_ms(gather, max(2, int(10 * reps_scale)), stream, cpm, chunk=10)
+        out[f"skewed_row_gather_{order}_nt_940MB"] = round(2 * n5 * row5 / (ms * 1e-3) / 1e12, 3)
+    del src5, dst5, perm5
     torch.cuda.empty_cache()
     return out
 
@@ -613,6 +630,16 @@ def summarize_ceilings(bench_json: str) -> str:
             "random permutation of the 1,024 rows of the buffer the copy before it wrote into (a row is read on another "
             "XCD than the one that wrote it 7 times in 8, as in the path), or through the identity, which keeps each "
             "row on its writer's XCD.", ""]
+    if "skewed_row_gather_permuted_nt_940MB" in c:
+        out += ["The skewed workload's streaming row gather: 65,536 rows of 14 KiB (940 MB), nontemporal loads and "
+                "stores, one-wave workgroups (as the library's streaming row kernels), 10 launches; each destination "
+                "row reads the source row a seeded random permutation names (the streaming reverse exchange's "
+                "pattern), or the same row (the identity):", "",
+                "| order | TB/s of bytes moved | of 8 TB/s |", "|---|---|---|"]
+        for order in ("identity", "permuted"):
+            v = c[f"skewed_row_gather_{order}_nt_940MB"]
+            out.append(f"| {order} | {v} | {v / 8:.3f} |")
+        out.append("")
     return "\n".join(out)
 
 

@@ -75,7 +75,10 @@ hipError_t launch_probe_copy(const void* src, void* dst, long long units, int po
 hipError_t launch_probe_gather(const void* src, int src_rows, void* dst, const int32_t* perm, int rows, int units,
                               int policy, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    const int B = pick_block(units);
+    // nontemporal gathers of streaming size run one-wave workgroups, as the
+    // library's streaming row kernels do; the rest the row-dividing size
+    const bool stream_shape = policy == 1 && (long long)rows * units * 16 >= kStreamingBytes;
+    const int B = stream_shape ? kStreamBlock : pick_block(units);
     const int slices = (units + B - 1) / B;
     auto kernel = policy == 1 ? probe_gather_kernel<1> : policy == 2 ? probe_gather_kernel<2> : probe_gather_kernel<0>;
     return launch_kernel(kernel, row_grid(rows, slices), dim3(B), 0, st, static_cast<const uint4*>(src),

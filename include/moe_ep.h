@@ -344,7 +344,9 @@ moe_status moe_stream_wait_event(void* stream, void* event);
  *                   equals 0xA5A5A5A5 (never, for a zero-filled source)
  *   moe_probe_gather  row r of dst (rows of row_bytes) = row perm[r] of src, for
  *                   r < rows, with the policies of moe_probe_copy; the
- *                   streaming exchange's pattern, so that a chain of such
+ *                   streaming exchange's pattern (nontemporal gathers of at
+ *                   least 128 MiB in one-wave workgroups, as the library's
+ *                   streaming row kernels), so that a chain of such
  *                   copies, each reading through a permutation what the one
  *                   before wrote, shows the cost of handing rows from one
  *                   kernel to the next in another order.  perm: device array

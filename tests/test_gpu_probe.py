@@ -28,7 +28,8 @@ def test_probe_copy_and_read(nbytes, policy):
     assert (sink == 0).all()
 
 
-@pytest.mark.parametrize("rows,row_bytes", [(1, 16), (577, 14336), (300, 4096 + 48)])
+@pytest.mark.parametrize("rows,row_bytes", [(1, 16), (577, 14336), (300, 4096 + 48),
+                                            (9400, 14336)])   # 135 MB: the streaming shape for nontemporal gathers
 @pytest.mark.parametrize("policy", [0, 1, 2])
 def test_probe_gather(rows, row_bytes, policy):
     import torch
