@@ -243,6 +243,23 @@ def test_extreme_skew_and_ties_in_logits(orc, E, k):
     _full_parity(orc, sh, wl.make_hidden(4, sh.T, H), logits=logits, label=f"skew+ties E={E}")
 
 
+@pytest.mark.parametrize("strength", [0.4, 1.0])
+def test_zipf_prior_in_identity_order(orc, strength):
+    """The skewed workload's Zipf log-prior -s*ln(1 + e) with the identity rank order: the hottest experts are
+    the lowest ids, which the contiguous placement puts on the first ranks, so one rank receives most of the
+    rows (at the skewed workload's strength 0.4: rank 0 about 7x the mean; at full strength 1.0 about 19x,
+    with many experts receiving nothing)."""
+    P, Tp, E, k, H = 32, 32, 256, 8, 256
+    sh = orc.Shape(P, P * Tp, E, k, H, True)
+    z = wl.normals(wl.stream_seed(0x5EED0007, wl.STREAM_LOGITS), sh.T * E).reshape(sh.T, E)
+    logits = (z - strength * np.log1p(np.arange(E, dtype=np.float64))[None, :]).astype(np.float32)
+    g, _ = _full_parity(orc, sh, wl.make_hidden(7, sh.T, H), logits=logits, label=f"zipf identity s={strength}")
+    per_rank = np.asarray(g["N"]).reshape(P, E // P).sum(axis=1)
+    assert per_rank[0] == per_rank.max() and per_rank[0] > 5 * per_rank.mean()
+    if strength == 1.0:
+        assert np.count_nonzero(np.asarray(g["N"]) == 0) > 50
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (32, 8), (96, 8), (256, 8)])
 def test_route_nan_logits(orc, E, k):
     """NaN logits rank below every number and tie with each other (lower id first), in
