@@ -49,3 +49,50 @@ def test_back_to_back_steps_stay_bit_identical(name, direct, steps):
     torch.cuda.synchronize()
     assert int(mismatches.item()) == 0, (name, direct, int(mismatches.item()))
     ctx.close()
+
+
+@pytest.mark.parametrize("name,parts,reps", [("c2", 2, 100), ("c3", 2, 50)])
+def test_two_stream_schedule_repeated_stays_bit_identical(name, parts, reps):
+    """The micro-batch schedule orders its two streams with the library's events; run many times back to
+    back (each run waits only for the comparisons of the one before), every micro-batch's routing, expert
+    outputs and y must keep the first run's bytes."""
+    import torch
+    from combine_router_softmax_expert_amd import binding as B
+
+    log(f"[repeat] two streams {name} parts={parts} reps={reps}")
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    P, Tp = w.num_ranks, w.tokens_per_rank
+    fp8 = w.dispatch_dtype != "bf16"
+    run = []
+    for c in range(parts):
+        rows = torch.from_numpy(wl.micro_batch_rows(P, Tp, parts, c)).cuda()
+        cc = B.Context(P, Tp // parts, w.num_experts, w.top_k, w.hidden, fp8)
+        run.append((cc, cc.allocate(), x[rows].contiguous(), logits[rows].contiguous()))
+    comm, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def once():
+        comm.wait_stream(main)                # the comparisons of the run before have read the outputs
+        compute.wait_stream(main)
+        B.run_overlapped(run, comm, compute)
+        main.wait_stream(comm)
+        main.wait_stream(compute)
+
+    keys = ("topk_ids", "topk_w", "expert_out", "y")
+    once()
+    torch.cuda.synchronize()
+    words = [{k: cb[k].view(torch.uint8).view(torch.int32) for k in keys} for _, cb, _, _ in run]
+    first = [{k: v.clone() for k, v in ws.items()} for ws in words]
+    mismatches = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(reps):
+        once()
+        for ws, fs in zip(words, first):
+            for k in keys:
+                mismatches += (ws[k] != fs[k]).sum()
+    torch.cuda.synchronize()
+    assert int(mismatches.item()) == 0, (name, int(mismatches.item()))
+    for cc, _, _, _ in run:
+        cc.close()
