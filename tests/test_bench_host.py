@@ -155,3 +155,29 @@ def test_cpu_baseline_reports_its_sample_cores_and_build(orc):
     m = re.match(r"(?:whole workload|first (\d+) of 64 tokens on each of 4 ranks) \((\d+) tokens\)", r["sample"])
     assert m, r["sample"]
     assert int(m.group(2)) == (256 if m.group(1) is None else 4 * int(m.group(1)))
+
+
+def test_ceilings_summary_renders_every_probe(tmp_path):
+    # a bench line with every ceiling key (values made up): the summary names each size and policy,
+    # the decode chains and, when present, the skewed row gather
+    c = {}
+    for label, _, _ in bench.CEILING_SIZES:
+        for kind in ("copy", "read"):
+            for tag in ("temporal", "nt", "write_through"):
+                c[f"{kind}_{tag}_{label}"] = 6.5
+    for tag in ("temporal", "nt", "write_through"):
+        c[f"decode_dc_four_copies_{tag}_us"] = 15.0
+        c[f"decode_dc_four_row_copies_permuted_{tag}_us"] = 17.5
+    c["decode_dc_four_row_copies_identity_write_through_us"] = 16.0
+    path = tmp_path / "bench.json"
+    path.write_text(json.dumps({"ceilings_tbps": c}) + "\n")
+    text = bench.summarize_ceilings(str(path))
+    for label, _, _ in bench.CEILING_SIZES:
+        assert f"| {label} |" in text
+    assert "random permutation | write-through | 17.5 |" in text
+    assert "skewed workload's streaming row gather" not in text
+    c["skewed_row_gather_identity_nt_940MB"] = 6.8
+    c["skewed_row_gather_permuted_nt_940MB"] = 6.3
+    path.write_text(json.dumps({"ceilings_tbps": c}) + "\n")
+    text = bench.summarize_ceilings(str(path))
+    assert "| permuted | 6.3 | 0.787 |" in text and "| identity | 6.8 | 0.850 |" in text
