@@ -69,10 +69,13 @@ typedef enum {
     MOE_DTYPE_FP8_E4M3 = 1      /* rows of H OCP E4M3 codes + H/128 fp32 scales */
 } moe_dtype;
 
-/* Problem shape.  Limits: 1 <= P; E % P == 0; E <= 1024; E/P <= 32767;
- * 1 <= k <= min(E, 32); H % 8 == 0 and 8 <= H; FP8 needs H % 128 == 0;
- * T * k < 2^31, T * k * (H/1024 + 1) < 2^31 and (T * k + P) * (H/8 + 512) < 2^32
- * (the grid of a row kernel). */
+/* Problem shape, with T = P * tokens_per_rank.  moe_ctx_create returns
+ * MOE_ERR_INVALID_ARG for P < 1, tokens_per_rank < 0, E < 1, E % P != 0,
+ * k < 1 or k > E, H < 8 or H % 8 != 0, or an unknown dispatch_dtype; and
+ * MOE_ERR_UNSUPPORTED, outside the supported limits, for E > 1024,
+ * E/P > 32767, k > 32, H > 65536, FP8 with H % 128 != 0, T * k >= 2^31,
+ * T * k * (H/1024 + 1) >= 2^31 or (T * k + P) * (H/8 + 512) >= 2^32 (the grid
+ * of a row kernel). */
 typedef struct {
     int32_t num_ranks;
     int32_t tokens_per_rank;
